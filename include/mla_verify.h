@@ -1,0 +1,142 @@
+/*
+ * mla_verify.h -- C ABI of libmla_verify.so: speculative-decoding verify
+ * attention for Multi-head Latent Attention (MLA) over a page_size = 1 latent
+ * KV cache, on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (magik.net, "The Decisive A/B": section "The Context: A Custom
+ * Kernel in Production"; "The Moment of Truth": opening section):
+ *   verify attention is the speculative-decoding step in which the target
+ *   model scores a block of drafted tokens in one pass.  MLA shares one latent
+ *   row per cached token among all heads; with page_size = 1 every token is its
+ *   own scattered slot of the pool, reached through a slot index.  For request
+ *   b with L = seq_lens[b] cached rows (its Q = q_lens[b] draft tokens
+ *   included, as the last Q of them), draft token t < Q and head h:
+ *     k_j   = kv_pool[slot_idx[ko_b + j]]          (576 bf16: 512 latent, 64 rope)
+ *     v_j   = k_j[0:512]
+ *     n_t   = L - Q + t + 1                        (causal within the draft block:
+ *                                                   draft t sees the prefix and
+ *                                                   drafts 0..t)
+ *     s_j   = sm_scale * dot(q[qo_b + t, h, :], k_j),   j < n_t
+ *     lse   = log(sum_j exp(s_j))                  (natural log, scale included)
+ *     out   = sum_j exp(s_j - lse) * v_j
+ *   where ko_b = sum of seq_lens before b and qo_b = sum of q_lens before b.
+ *   It is computed the way the pages' kernel does, as a KV split with a
+ *   partial result per chunk of keys followed by a reduce of the partials
+ *   ("The Decisive A/B": "The Context" and "What This Reveals About the
+ *   Bottleneck"), with a fixed split count and preallocated workspace so that
+ *   a call can be captured in a HIP graph (same page, "The Context").
+ *
+ * Conventions for every entry point:
+ *   - Return value: MLA_OK (0) or a negative MLA_ERR_* status.  No exception
+ *     or signal crosses the ABI.  mla_verify_error_string() names a status.
+ *   - Pointers marked "device" must be device memory of the current HIP device;
+ *     the caller owns them and keeps them alive until the stream has passed
+ *     the call.  Host-visible arguments are validated before any HIP call.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Work is enqueued asynchronously; nothing is allocated, copied or
+ *     synchronised by the run/merge calls, so they may be captured in a graph.
+ *   - Values the library cannot see from the host (contents of seq_lens,
+ *     q_lens, slot_idx) must satisfy the stated ranges; violations are
+ *     undefined behaviour except where a clamp is stated.
+ */
+#ifndef MLA_VERIFY_H
+#define MLA_VERIFY_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLA_OK 0
+#define MLA_ERR_INVALID_ARGUMENT (-1) /* null pointer, bad size, misaligned pointer, nsplit out of range */
+#define MLA_ERR_UNSUPPORTED (-2)      /* d_qk != 576 or d_v != 512 */
+#define MLA_ERR_OUT_OF_MEMORY (-3)    /* workspace allocation failed */
+#define MLA_ERR_HIP (-4)              /* a HIP runtime call or a kernel launch failed, or no GPU */
+
+#define MLA_VERIFY_D_QK 576 /* 512 latent + 64 rope dims per cached row and per query */
+#define MLA_VERIFY_D_V 512  /* v is the first 512 dims of each cached row */
+
+typedef struct mla_verify_s* mla_verify_handle; /* opaque */
+
+/* Shapes fixed for the life of a handle (a captured graph sees the same shapes). */
+typedef struct {
+  int32_t num_heads;  /* H >= 1 */
+  int32_t d_qk;       /* must be 576 */
+  int32_t d_v;        /* must be 512 */
+  int32_t batch;      /* B >= 1: number of requests per call */
+  int32_t max_q_len;  /* Q_max >= 1: upper bound on every q_lens[b] */
+  int32_t max_nsplit; /* >= 1: the workspace holds this many partials per row */
+  int64_t num_slots;  /* rows in kv_pool (>= 1) */
+  float sm_scale;     /* score scale, > 0 (1/sqrt(192) in the reference workloads) */
+} mla_verify_config;
+
+/*
+ * Validate `cfg`, allocate the split workspace on the current device
+ * (B * max_nsplit * ceil(Q_max*H/128)*128 rows of 512 fp32 plus one fp32
+ * log-sum-exp each) and return a handle in *out.  Call outside graph capture.
+ * Errors: INVALID_ARGUMENT (null, non-positive sizes), UNSUPPORTED (dims),
+ * OUT_OF_MEMORY, HIP (no device).  On error *out is set to NULL.
+ */
+int mla_verify_create(const mla_verify_config* cfg, mla_verify_handle* out);
+
+/*
+ * One verify-attention call: split partials (kernel 1) then their merge
+ * (kernel 2), both on `stream`.
+ *   q        device bf16 [T_q, H, 576], T_q = sum(q_lens), requests in order,
+ *            rows 16-byte aligned (base pointer 16-byte aligned).
+ *   kv_pool  device bf16 [num_slots, 576], row stride 1152 bytes, 16-byte aligned.
+ *   slot_idx device int32 [sum(seq_lens)]: request b's L_b slots in key order
+ *            (its draft rows last); each 0 <= slot < num_slots.
+ *   seq_lens device int32 [B], L_b >= 0.
+ *   q_lens   device int32 [B], 0 <= Q_b <= min(L_b, max_q_len).  Q_b = 0 writes
+ *            nothing for request b.  Q_b is clamped to that range on the device.
+ *   out      device bf16 [T_q, H, 512], 16-byte aligned (written, round to nearest even).
+ *   lse      device fp32 [T_q, H] (written; natural log; -inf only if no key is visible).
+ *   nsplit   1 <= nsplit <= max_nsplit.  The keys of each request are divided
+ *            into at most nsplit contiguous chunks; the result does not depend
+ *            on nsplit beyond rounding.  Keep it constant across replays of a
+ *            captured graph.
+ * The handle's workspace is reused by every call: calls on one handle must
+ * not overlap (serialise them on one stream).  Distinct handles are independent.
+ */
+int mla_verify_run(mla_verify_handle h, const void* q, const void* kv_pool, const int32_t* slot_idx,
+                   const int32_t* seq_lens, const int32_t* q_lens, void* out, float* lse, int32_t nsplit,
+                   void* stream);
+
+/*
+ * Kernel 1 alone: the split partials of one call, left in the handle's
+ * workspace (the "partial" half of the pages' partial + reduce).  Arguments
+ * as in mla_verify_run.  mla_verify_run is this call followed by the merge;
+ * this entry exists to time and inspect the partial phase by itself.
+ */
+int mla_verify_partials(mla_verify_handle h, const void* q, const void* kv_pool, const int32_t* slot_idx,
+                        const int32_t* seq_lens, const int32_t* q_lens, int32_t nsplit, void* stream);
+
+/*
+ * Kernel 2 alone: merge caller-provided split partials (the reduce of the
+ * pages' partial + reduce scheme).  Every one of the nsplit partials of a row
+ * takes part; a partial with lse = -inf carries no weight.
+ *   o_part   device fp32 [batch, nsplit, max_q_len * H, 512]: partial outputs,
+ *            each already normalised within its chunk; row r of request b is
+ *            (token r / H, head r % H).  16-byte aligned.
+ *   lse_part device fp32 [batch, nsplit, max_q_len * H]: natural-log LSE per chunk.
+ *   q_lens   device int32 [batch] (same clamp as in mla_verify_run).
+ *   out, lse as in mla_verify_run.
+ * Errors: INVALID_ARGUMENT, HIP.
+ */
+int mla_verify_merge(const float* o_part, const float* lse_part, const int32_t* q_lens, int32_t batch,
+                     int32_t num_heads, int32_t max_q_len, int32_t nsplit, void* out, float* lse, void* stream);
+
+/* Free the workspace and the handle.  NULL is a no-op.  The caller must make
+ * sure no enqueued call still uses the handle (synchronise its stream first). */
+int mla_verify_destroy(mla_verify_handle h);
+
+/* Static, NUL-terminated name of a status code; never NULL. */
+const char* mla_verify_error_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_VERIFY_H */

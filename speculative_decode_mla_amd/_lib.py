@@ -1,0 +1,81 @@
+"""ctypes view of libmla_verify.so (the C ABI declared in include/mla_verify.h).
+
+Argument marshalling only.  Loading fails loudly if the library is not built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla_verify.so")
+
+MLA_OK = 0
+MLA_ERR_INVALID_ARGUMENT = -1
+MLA_ERR_UNSUPPORTED = -2
+MLA_ERR_OUT_OF_MEMORY = -3
+MLA_ERR_HIP = -4
+
+D_QK = 576
+D_V = 512
+
+# Every function the header declares, with its ctypes signature.
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+
+
+class MlaVerifyConfig(ctypes.Structure):
+    _fields_ = [
+        ("num_heads", ctypes.c_int32),
+        ("d_qk", ctypes.c_int32),
+        ("d_v", ctypes.c_int32),
+        ("batch", ctypes.c_int32),
+        ("max_q_len", ctypes.c_int32),
+        ("max_nsplit", ctypes.c_int32),
+        ("num_slots", ctypes.c_int64),
+        ("sm_scale", ctypes.c_float),
+    ]
+
+
+SIGNATURES = {
+    "mla_verify_create": (ctypes.c_int, [ctypes.POINTER(MlaVerifyConfig), ctypes.POINTER(_P)]),
+    "mla_verify_run": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _P]),
+    "mla_verify_partials": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I32, _P]),
+    "mla_verify_merge": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _P]),
+    "mla_verify_destroy": (ctypes.c_int, [_P]),
+    "mla_verify_error_string": (ctypes.c_char_p, [ctypes.c_int]),
+}
+
+_lib = None
+
+
+class MlaVerifyError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {error_string(status)} ({status})")
+        self.status = status
+
+
+def load() -> ctypes.CDLL:
+    """Load the library once.  Import torch before calling this on a GPU so that
+    the library binds to the HIP runtime torch already loaded."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"{LIB_PATH} is not built; run `python -m speculative_decode_mla_amd.build` "
+                "(there is no fallback implementation)")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def error_string(status: int) -> str:
+    return load().mla_verify_error_string(status).decode()
+
+
+def check(fn: str, status: int) -> None:
+    if status != MLA_OK:
+        raise MlaVerifyError(fn, status)

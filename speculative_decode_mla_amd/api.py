@@ -1,0 +1,135 @@
+"""Torch-facing binding of the MLA verify-attention library.
+
+PyTorch supplies device memory and the stream; every step of the computation
+runs in the HIP kernels of libmla_verify.so.  Functions here only check shapes
+and dtypes on the host and pass raw pointers through the C ABI.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+
+import torch
+
+from . import _lib
+
+D_QK = _lib.D_QK
+D_V = _lib.D_V
+DEFAULT_SCALE = 1.0 / math.sqrt(192.0)
+
+
+def _ptr(t: torch.Tensor) -> ctypes.c_void_p:
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_handle(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype, dim: int):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != dim:
+        raise ValueError(f"{name} must have {dim} dims, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU, got {t.device}")
+
+
+class MlaVerify:
+    """A handle: shapes fixed at creation, split workspace owned by the library.
+
+    run() enqueues the two kernels on the current (or given) stream and returns
+    without synchronising, so it can be captured in a torch.cuda.CUDAGraph.
+    """
+
+    def __init__(self, num_heads: int, batch: int, max_q_len: int, max_nsplit: int, num_slots: int,
+                 sm_scale: float = DEFAULT_SCALE):
+        lib = _lib.load()
+        self.cfg = _lib.MlaVerifyConfig(num_heads, D_QK, D_V, batch, max_q_len, max_nsplit, num_slots, sm_scale)
+        h = ctypes.c_void_p()
+        _lib.check("mla_verify_create", lib.mla_verify_create(ctypes.byref(self.cfg), ctypes.byref(h)))
+        self._h = h
+        self.num_heads, self.batch, self.max_q_len = num_heads, batch, max_q_len
+        self.max_nsplit, self.num_slots = max_nsplit, num_slots
+
+    def close(self):
+        if getattr(self, "_h", None) is not None and self._h.value is not None:
+            _lib.check("mla_verify_destroy", _lib.load().mla_verify_destroy(self._h))
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def _check_inputs(self, q, kv_pool, slot_idx, seq_lens, q_lens):
+        H = self.num_heads
+        _need(q, "q", torch.bfloat16, 3)
+        _need(kv_pool, "kv_pool", torch.bfloat16, 2)
+        _need(slot_idx, "slot_idx", torch.int32, 1)
+        _need(seq_lens, "seq_lens", torch.int32, 1)
+        _need(q_lens, "q_lens", torch.int32, 1)
+        if q.shape[1:] != (H, D_QK):
+            raise ValueError(f"q must be [T_q, {H}, {D_QK}], got {tuple(q.shape)}")
+        if kv_pool.shape[1] != D_QK or kv_pool.shape[0] > self.num_slots:
+            raise ValueError(f"kv_pool must be [<= {self.num_slots}, {D_QK}], got {tuple(kv_pool.shape)}")
+        if seq_lens.shape[0] != self.batch or q_lens.shape[0] != self.batch:
+            raise ValueError(f"seq_lens and q_lens must have {self.batch} entries")
+
+    def partials(self, q, kv_pool, slot_idx, seq_lens, q_lens, nsplit: int, stream=None):
+        """Kernel 1 only: split partials into the handle's workspace."""
+        self._check_inputs(q, kv_pool, slot_idx, seq_lens, q_lens)
+        st = _lib.load().mla_verify_partials(self._h, _ptr(q), _ptr(kv_pool), _ptr(slot_idx), _ptr(seq_lens),
+                                             _ptr(q_lens), int(nsplit), _stream_handle(stream))
+        _lib.check("mla_verify_partials", st)
+
+    def run(self, q, kv_pool, slot_idx, seq_lens, q_lens, out, lse, nsplit: int, stream=None):
+        """out[T_q, H, 512] (bf16) and lse[T_q, H] (fp32) for one verify step."""
+        H = self.num_heads
+        _need(q, "q", torch.bfloat16, 3)
+        _need(kv_pool, "kv_pool", torch.bfloat16, 2)
+        _need(slot_idx, "slot_idx", torch.int32, 1)
+        _need(seq_lens, "seq_lens", torch.int32, 1)
+        _need(q_lens, "q_lens", torch.int32, 1)
+        _need(out, "out", torch.bfloat16, 3)
+        _need(lse, "lse", torch.float32, 2)
+        if q.shape[1:] != (H, D_QK):
+            raise ValueError(f"q must be [T_q, {H}, {D_QK}], got {tuple(q.shape)}")
+        if kv_pool.shape[1] != D_QK or kv_pool.shape[0] > self.num_slots:
+            raise ValueError(f"kv_pool must be [<= {self.num_slots}, {D_QK}], got {tuple(kv_pool.shape)}")
+        if seq_lens.shape[0] != self.batch or q_lens.shape[0] != self.batch:
+            raise ValueError(f"seq_lens and q_lens must have {self.batch} entries")
+        if out.shape != (q.shape[0], H, D_V):
+            raise ValueError(f"out must be [{q.shape[0]}, {H}, {D_V}], got {tuple(out.shape)}")
+        if lse.shape != (q.shape[0], H):
+            raise ValueError(f"lse must be [{q.shape[0]}, {H}], got {tuple(lse.shape)}")
+        st = _lib.load().mla_verify_run(self._h, _ptr(q), _ptr(kv_pool), _ptr(slot_idx), _ptr(seq_lens), _ptr(q_lens),
+                                        _ptr(out), _ptr(lse), int(nsplit), _stream_handle(stream))
+        _lib.check("mla_verify_run", st)
+        return out, lse
+
+
+def merge(o_part, lse_part, q_lens, out, lse, stream=None):
+    """Kernel 2 alone: reduce caller-provided split partials.
+
+    o_part fp32 [B, S, max_q_len*H, 512], lse_part fp32 [B, S, max_q_len*H] (natural log).
+    """
+    _need(o_part, "o_part", torch.float32, 4)
+    _need(lse_part, "lse_part", torch.float32, 3)
+    _need(q_lens, "q_lens", torch.int32, 1)
+    _need(out, "out", torch.bfloat16, 3)
+    _need(lse, "lse", torch.float32, 2)
+    B, S, rows, dv = o_part.shape
+    H = out.shape[1]
+    if dv != D_V or rows % H or lse_part.shape != (B, S, rows) or q_lens.shape[0] != B:
+        raise ValueError("inconsistent partial shapes")
+    st = _lib.load().mla_verify_merge(_ptr(o_part), _ptr(lse_part), _ptr(q_lens), B, H, rows // H, S,
+                                      _ptr(out), _ptr(lse), _stream_handle(stream))
+    _lib.check("mla_verify_merge", st)
+    return out, lse

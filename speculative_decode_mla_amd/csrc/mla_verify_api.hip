@@ -1,0 +1,191 @@
+// C ABI of libmla_verify.so (declared in include/mla_verify.h): argument
+// checks, workspace ownership and the two launches of a verify call.
+#include "mla_verify.h"
+
+#include <cmath>
+#include <cstdint>
+#include <new>
+
+#include "mla_verify_internal.h"
+
+struct mla_verify_s {
+  mla_verify_config cfg;
+  int device;
+  int32_t row_groups;
+  int32_t rows_pad;
+  float* o_part;    // [B, max_nsplit, rows_pad, 512]
+  float* lse_part;  // [B, max_nsplit, rows_pad]
+};
+
+namespace {
+
+// Splits are given at least this many 64-key tiles, so a short request does not
+// fan out into many tiny partials (the result does not depend on the split count).
+constexpr int32_t kMinTilesPerSplit = 4;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return MLA_OK;
+  return e == hipErrorOutOfMemory ? MLA_ERR_OUT_OF_MEMORY : MLA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_verify_error_string(int status) {
+  switch (status) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_ERR_INVALID_ARGUMENT: return "MLA_ERR_INVALID_ARGUMENT";
+    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED";
+    case MLA_ERR_OUT_OF_MEMORY: return "MLA_ERR_OUT_OF_MEMORY";
+    case MLA_ERR_HIP: return "MLA_ERR_HIP";
+    default: return "MLA_ERR_UNKNOWN";
+  }
+}
+
+int mla_verify_create(const mla_verify_config* cfg, mla_verify_handle* out) {
+  if (out == nullptr) return MLA_ERR_INVALID_ARGUMENT;
+  *out = nullptr;
+  if (cfg == nullptr) return MLA_ERR_INVALID_ARGUMENT;
+  if (cfg->num_heads < 1 || cfg->batch < 1 || cfg->max_q_len < 1 || cfg->max_nsplit < 1 || cfg->num_slots < 1)
+    return MLA_ERR_INVALID_ARGUMENT;
+  if (!(cfg->sm_scale > 0.f) || !std::isfinite(cfg->sm_scale)) return MLA_ERR_INVALID_ARGUMENT;
+  if (cfg->d_qk != MLA_VERIFY_D_QK || cfg->d_v != MLA_VERIFY_D_V) return MLA_ERR_UNSUPPORTED;
+  const int64_t rows = (int64_t)cfg->max_q_len * cfg->num_heads;
+  const int64_t row_groups = (rows + mlav::kRowsPerGroup - 1) / mlav::kRowsPerGroup;
+  const int64_t rows_pad = row_groups * mlav::kRowsPerGroup;
+  const int64_t grid = (int64_t)cfg->batch * cfg->max_nsplit * row_groups;
+  if (rows_pad > INT32_MAX / 2 || grid > INT32_MAX || (int64_t)cfg->batch * rows > INT32_MAX)
+    return MLA_ERR_INVALID_ARGUMENT;
+
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MLA_ERR_HIP;
+  const int64_t partial_rows = (int64_t)cfg->batch * cfg->max_nsplit * rows_pad;
+  mla_verify_s* h = new (std::nothrow) mla_verify_s();
+  if (h == nullptr) return MLA_ERR_OUT_OF_MEMORY;
+  h->cfg = *cfg;
+  h->device = dev;
+  h->row_groups = (int32_t)row_groups;
+  h->rows_pad = (int32_t)rows_pad;
+  int st = hip_status(hipMalloc((void**)&h->o_part, (size_t)partial_rows * mlav::kDv * sizeof(float)));
+  if (st == MLA_OK) st = hip_status(hipMalloc((void**)&h->lse_part, (size_t)partial_rows * sizeof(float)));
+  if (st != MLA_OK) {
+    (void)hipGetLastError();
+    mla_verify_destroy(h);
+    return st;
+  }
+  *out = h;
+  return MLA_OK;
+}
+
+namespace {
+
+int check_run_args(mla_verify_handle h, const void* q, const void* kv_pool, const int32_t* slot_idx,
+                   const int32_t* seq_lens, const int32_t* q_lens, int32_t nsplit) {
+  if (h == nullptr || q == nullptr || kv_pool == nullptr || slot_idx == nullptr || seq_lens == nullptr ||
+      q_lens == nullptr)
+    return MLA_ERR_INVALID_ARGUMENT;
+  if (nsplit < 1 || nsplit > h->cfg.max_nsplit) return MLA_ERR_INVALID_ARGUMENT;
+  if (!aligned(q, 16) || !aligned(kv_pool, 16) || !aligned(slot_idx, 4) || !aligned(seq_lens, 4) ||
+      !aligned(q_lens, 4))
+    return MLA_ERR_INVALID_ARGUMENT;
+  return MLA_OK;
+}
+
+int launch_partials(mla_verify_handle h, const void* q, const void* kv_pool, const int32_t* slot_idx,
+                    const int32_t* seq_lens, const int32_t* q_lens, int32_t nsplit, hipStream_t s) {
+  const mla_verify_config& c = h->cfg;
+  mlav::PartialArgs pa;
+  pa.q = static_cast<const uint16_t*>(q);
+  pa.kv = static_cast<const uint16_t*>(kv_pool);
+  pa.slot_idx = slot_idx;
+  pa.seq_lens = seq_lens;
+  pa.q_lens = q_lens;
+  pa.o_part = h->o_part;
+  pa.lse_part = h->lse_part;
+  pa.batch = c.batch;
+  pa.heads = c.num_heads;
+  pa.max_q_len = c.max_q_len;
+  pa.nsplit = nsplit;
+  pa.row_groups = h->row_groups;
+  pa.rows_pad = h->rows_pad;
+  pa.min_tiles = kMinTilesPerSplit;
+  pa.scale_log2 = c.sm_scale * 1.4426950408889634f;
+  return mlav::launch_partial(pa, s) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+}  // namespace
+
+int mla_verify_partials(mla_verify_handle h, const void* q, const void* kv_pool, const int32_t* slot_idx,
+                        const int32_t* seq_lens, const int32_t* q_lens, int32_t nsplit, void* stream) {
+  int st = check_run_args(h, q, kv_pool, slot_idx, seq_lens, q_lens, nsplit);
+  if (st != MLA_OK) return st;
+  return launch_partials(h, q, kv_pool, slot_idx, seq_lens, q_lens, nsplit, static_cast<hipStream_t>(stream));
+}
+
+int mla_verify_run(mla_verify_handle h, const void* q, const void* kv_pool, const int32_t* slot_idx,
+                   const int32_t* seq_lens, const int32_t* q_lens, void* out, float* lse, int32_t nsplit,
+                   void* stream) {
+  int st = check_run_args(h, q, kv_pool, slot_idx, seq_lens, q_lens, nsplit);
+  if (st != MLA_OK) return st;
+  if (out == nullptr || lse == nullptr || !aligned(out, 16) || !aligned(lse, 4)) return MLA_ERR_INVALID_ARGUMENT;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = launch_partials(h, q, kv_pool, slot_idx, seq_lens, q_lens, nsplit, s);
+  if (st != MLA_OK) return st;
+
+  const mla_verify_config& c = h->cfg;
+  mlav::MergeArgs ma;
+  ma.o_part = h->o_part;
+  ma.lse_part = h->lse_part;
+  ma.seq_lens = seq_lens;
+  ma.q_lens = q_lens;
+  ma.out = static_cast<uint16_t*>(out);
+  ma.lse = lse;
+  ma.batch = c.batch;
+  ma.heads = c.num_heads;
+  ma.max_q_len = c.max_q_len;
+  ma.nsplit = nsplit;
+  ma.rows_stride = h->rows_pad;
+  ma.min_tiles = kMinTilesPerSplit;
+  ma.use_all_splits = 0;
+  return mlav::launch_merge(ma, s) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+int mla_verify_merge(const float* o_part, const float* lse_part, const int32_t* q_lens, int32_t batch,
+                     int32_t num_heads, int32_t max_q_len, int32_t nsplit, void* out, float* lse, void* stream) {
+  if (o_part == nullptr || lse_part == nullptr || q_lens == nullptr || out == nullptr || lse == nullptr)
+    return MLA_ERR_INVALID_ARGUMENT;
+  if (batch < 1 || num_heads < 1 || max_q_len < 1 || nsplit < 1) return MLA_ERR_INVALID_ARGUMENT;
+  if ((int64_t)max_q_len * num_heads * batch > INT32_MAX) return MLA_ERR_INVALID_ARGUMENT;
+  if (!aligned(o_part, 16) || !aligned(out, 16) || !aligned(lse_part, 4) || !aligned(lse, 4) ||
+      !aligned(q_lens, 4))
+    return MLA_ERR_INVALID_ARGUMENT;
+  mlav::MergeArgs ma;
+  ma.o_part = o_part;
+  ma.lse_part = lse_part;
+  ma.seq_lens = nullptr;
+  ma.q_lens = q_lens;
+  ma.out = static_cast<uint16_t*>(out);
+  ma.lse = lse;
+  ma.batch = batch;
+  ma.heads = num_heads;
+  ma.max_q_len = max_q_len;
+  ma.nsplit = nsplit;
+  ma.rows_stride = max_q_len * num_heads;
+  ma.min_tiles = 1;
+  ma.use_all_splits = 1;
+  return hip_status(mlav::launch_merge(ma, static_cast<hipStream_t>(stream))) == MLA_OK ? MLA_OK : MLA_ERR_HIP;
+}
+
+int mla_verify_destroy(mla_verify_handle h) {
+  if (h == nullptr) return MLA_OK;
+  int st = MLA_OK;
+  if (h->o_part != nullptr && hipFree(h->o_part) != hipSuccess) st = MLA_ERR_HIP;
+  if (h->lse_part != nullptr && hipFree(h->lse_part) != hipSuccess) st = MLA_ERR_HIP;
+  delete h;
+  return st;
+}
+
+}  // extern "C"

@@ -1,0 +1,49 @@
+// Internal launch interface between the C-ABI layer and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mlav {
+
+// Geometry shared by the host planner and the kernels.
+constexpr int kDqk = 576;            // 512 latent + 64 rope dims
+constexpr int kDv = 512;             // v = first 512 dims of a latent row
+constexpr int kRowBytes = kDqk * 2;  // one bf16 latent row: 1152 B = 9 x 128-B lines
+constexpr int kWaves = 4;            // waves per workgroup (one per SIMD)
+constexpr int kRowsPerWave = 32;     // (token, head) rows owned by one wave
+constexpr int kRowsPerGroup = kWaves * kRowsPerWave;  // rows per workgroup: 128
+constexpr int kTileKeys = 64;        // keys gathered into LDS per step
+
+// Kernel 1: one workgroup per (request, split, 128-row group).
+struct PartialArgs {
+  const uint16_t* q;         // bf16 [T_q*H, 576]
+  const uint16_t* kv;        // bf16 [num_slots, 576]
+  const int32_t* slot_idx;   // [sum L]
+  const int32_t* seq_lens;   // [B]
+  const int32_t* q_lens;     // [B]
+  float* o_part;             // fp32 [B, nsplit, rows_pad, 512]
+  float* lse_part;           // fp32 [B, nsplit, rows_pad], natural log
+  int32_t batch, heads, max_q_len, nsplit;
+  int32_t row_groups;        // ceil(max_q_len*H / 128)
+  int32_t rows_pad;          // row_groups * 128
+  int32_t min_tiles;         // fewest 64-key tiles a split is given (caps the split count)
+  float scale_log2;          // sm_scale * log2(e)
+};
+
+// Kernel 2: one wave per (request, row); merges the row's split partials.
+struct MergeArgs {
+  const float* o_part;       // fp32 [B, nsplit, rows_stride, 512]
+  const float* lse_part;     // fp32 [B, nsplit, rows_stride]
+  const int32_t* seq_lens;   // [B]; read only when use_all_splits == 0
+  const int32_t* q_lens;     // [B]
+  uint16_t* out;             // bf16 [T_q*H, 512]
+  float* lse;                // fp32 [T_q*H]
+  int32_t batch, heads, max_q_len, nsplit, rows_stride, min_tiles;
+  int32_t use_all_splits;    // 1: merge all nsplit partials; 0: only the splits kernel 1 filled
+};
+
+hipError_t launch_partial(const PartialArgs& a, hipStream_t stream);
+hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
+
+}  // namespace mlav

@@ -90,6 +90,26 @@ class VerifyInputs:
         pool[self.slot_idx] = self.kv_rows
         return pool
 
+    def sparse_pool(self) -> "SparsePool":
+        """The same pool without materialising the unreferenced rows (for large pools)."""
+        return SparsePool(self.kv_rows, self.slot_idx, self.num_slots)
+
+
+class SparsePool:
+    """Indexable like the host pool (pool[slots] -> rows); unreferenced slots read as NaN rows."""
+
+    def __init__(self, kv_rows: np.ndarray, slot_idx: np.ndarray, num_slots: int):
+        self.kv_rows = kv_rows
+        self.row_of_slot = np.full(num_slots, -1, dtype=np.int64)
+        self.row_of_slot[slot_idx] = np.arange(len(slot_idx))
+        self.shape = (num_slots, D_QK)
+
+    def __getitem__(self, slots):
+        r = self.row_of_slot[np.asarray(slots, dtype=np.int64)]
+        out = self.kv_rows[np.maximum(r, 0)]
+        out[r < 0] = BF16_QNAN
+        return out
+
 
 def ragged_lengths(rng: np.random.Generator, batch: int, lo: int, hi: int) -> np.ndarray:
     return np.rint(np.exp(rng.uniform(math.log(lo), math.log(hi), batch))).astype(np.int64)

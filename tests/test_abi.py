@@ -1,0 +1,88 @@
+"""The C-ABI library loads and exports what include/mla_verify.h declares (no GPU calls)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from speculative_decode_mla_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla_verify.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(mla_verify_\w+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.skip("library not built")
+    return _lib.load()
+
+
+def test_header_declares_the_boundary():
+    assert _declared() == ["mla_verify_create", "mla_verify_destroy", "mla_verify_error_string",
+                           "mla_verify_merge", "mla_verify_partials", "mla_verify_run"]
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (mla_verify_\w+)$", out, re.M))
+    assert set(_declared()) <= exported
+    assert set(_declared()) == set(_lib.SIGNATURES)
+    for name in _declared():
+        assert hasattr(lib, name)
+
+
+def test_config_struct_layout_matches_header():
+    assert ctypes.sizeof(_lib.MlaVerifyConfig) == 40
+    assert _lib.MlaVerifyConfig.num_slots.offset == 24 and _lib.MlaVerifyConfig.sm_scale.offset == 32
+
+
+def test_error_strings(lib):
+    assert _lib.error_string(0) == "MLA_OK"
+    assert _lib.error_string(-1) == "MLA_ERR_INVALID_ARGUMENT"
+    assert _lib.error_string(-4) == "MLA_ERR_HIP"
+    assert _lib.error_string(12345) == "MLA_ERR_UNKNOWN"
+
+
+def test_host_validation_before_any_hip_call(lib):
+    P = ctypes.c_void_p
+    assert lib.mla_verify_run(None, None, None, None, None, None, None, None, 1, None) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert lib.mla_verify_merge(None, None, None, 1, 1, 1, 1, None, None, None) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert lib.mla_verify_partials(None, None, None, None, None, None, 1, None) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert lib.mla_verify_destroy(None) == _lib.MLA_OK
+    h = P()
+    assert lib.mla_verify_create(None, ctypes.byref(h)) == _lib.MLA_ERR_INVALID_ARGUMENT
+    bad = _lib.MlaVerifyConfig(16, 512, 512, 1, 4, 1, 4096, 0.07)
+    assert lib.mla_verify_create(ctypes.byref(bad), ctypes.byref(h)) == _lib.MLA_ERR_UNSUPPORTED
+    bad = _lib.MlaVerifyConfig(0, 576, 512, 1, 4, 1, 4096, 0.07)
+    assert lib.mla_verify_create(ctypes.byref(bad), ctypes.byref(h)) == _lib.MLA_ERR_INVALID_ARGUMENT
+    bad = _lib.MlaVerifyConfig(16, 576, 512, 1, 4, 1, 4096, float("nan"))
+    assert lib.mla_verify_create(ctypes.byref(bad), ctypes.byref(h)) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert h.value is None
+
+
+def test_create_without_a_gpu_reports_hip_error(lib):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    h = ctypes.c_void_p()
+    cfg = _lib.MlaVerifyConfig(16, 576, 512, 1, 4, 1, 4096, 0.07)
+    assert lib.mla_verify_create(ctypes.byref(cfg), ctypes.byref(h)) == _lib.MLA_ERR_HIP
+    assert h.value is None
+
+
+def test_torch_wrapper_rejects_bad_tensors():
+    import torch
+    from speculative_decode_mla_amd import api
+    with pytest.raises(ValueError):
+        api._need(torch.zeros(3, dtype=torch.float32), "x", torch.bfloat16, 1)
+    with pytest.raises(ValueError):
+        api._need(torch.zeros(3, 4, dtype=torch.bfloat16).t(), "x", torch.bfloat16, 2)
+    with pytest.raises(ValueError):
+        api._need(torch.zeros(3, dtype=torch.bfloat16), "x", torch.bfloat16, 1)  # not on a GPU

@@ -1,0 +1,225 @@
+"""GPU parity: the HIP path against the fp64 oracle on the same seeded inputs.
+
+Bar (from the tolerance on bf16 outputs and fp32 log-sum-exp): max |out err| <= 1e-2,
+max |lse err| <= 1e-3, element by element.  All calls go through the C ABI.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from speculative_decode_mla_amd import inputs as I
+from tests.gpu_helpers import LSE_TOL, OUT_TOL, DeviceInputs, bf16_to_f64, bits_to_bf16, max_errors
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def api():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from speculative_decode_mla_amd import api as A
+    return A
+
+
+def _handle(api, x, nsplit, max_q=None):
+    return api.MlaVerify(x.heads, len(x.seq_lens), max_q or int(max(1, x.q_lens.max())), nsplit, x.num_slots, x.scale)
+
+
+def _check(api, x, nsplit, label=""):
+    d = DeviceInputs(x)
+    h = _handle(api, x, nsplit)
+    out, lse = d.run(h, nsplit)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle.verify_attention(x.q, x.pool(), x.slot_idx, x.seq_lens, x.q_lens, x.scale)
+    eo, el = max_errors(out, lse, ref_o, ref_l)
+    print(f"{label} nsplit={nsplit}: max|out err|={eo:.3e} max|lse err|={el:.3e}", flush=True)
+    assert eo <= OUT_TOL and el <= LSE_TOL
+    return d, h
+
+
+def test_tiny_workload(api):
+    _check(api, I.make_inputs("tiny"), 1, "tiny")
+
+
+CASES = [
+    # (seed, seq_lens, q_lens, heads, nsplit)
+    (20, [1000], [8], 64, 4),
+    (21, [130, 64, 1, 700], [3, 1, 1, 16], 8, 3),
+    (22, [65], [4], 2, 2),              # the second split holds only draft keys: fully masked rows
+    (23, [1], [1], 64, 1),              # one key: out is that v row
+    (24, [50, 20], [0, 5], 16, 2),      # a request with no draft tokens
+    (25, [300], [7], 5, 2),             # 35 rows: a partly filled wave
+    (26, [300], [16], 64, 2),           # 1024 rows: eight row groups
+    (27, [4096 + 37], [16], 16, 8),     # ragged last tile
+    (28, [64, 128, 192], [16, 16, 16], 4, 32),  # more splits than tiles
+]
+
+
+@pytest.mark.parametrize("seed,lens,qlens,heads,nsplit", CASES)
+def test_small_cases(api, seed, lens, qlens, heads, nsplit):
+    x = I.make_custom(np.random.default_rng(seed), lens, qlens, heads, int(sum(lens)) * 2 + 64)
+    _check(api, x, nsplit, f"case{seed}")
+
+
+def test_ctx4k_workload(api):
+    _check(api, I.make_inputs("ctx4k"), 8, "ctx4k")
+
+
+def test_single_key_is_exact(api):
+    x = I.make_custom(np.random.default_rng(30), [1], [1], 64, 100)
+    d = DeviceInputs(x)
+    out, lse = d.run(_handle(api, x, 1), 1)
+    torch.cuda.synchronize()
+    v = torch.from_numpy(x.kv_rows[0, :512].view(np.int16).copy()).view(torch.bfloat16)
+    assert torch.equal(out.cpu()[0], v.expand(64, 512))
+
+
+def test_split_count_does_not_change_result(api):
+    x = I.make_custom(np.random.default_rng(31), [3000, 900], [16, 9], 32, 10000)
+    d = DeviceInputs(x)
+    h = _handle(api, x, 32)
+    ref_o, ref_l = oracle.verify_attention(x.q, x.pool(), x.slot_idx, x.seq_lens, x.q_lens, x.scale)
+    outs = []
+    for ns in (1, 2, 5, 32, 7):
+        out, lse = d.run(h, ns)
+        torch.cuda.synchronize()
+        eo, el = max_errors(out, lse, ref_o, ref_l)
+        assert eo <= OUT_TOL and el <= LSE_TOL, (ns, eo, el)
+        outs.append(bf16_to_f64(out))
+    assert max(np.max(np.abs(o - outs[0])) for o in outs) <= OUT_TOL
+
+
+def test_slot_permutation_is_bitwise(api):
+    x = I.make_custom(np.random.default_rng(32), [777, 300], [8, 8], 16, 5000)
+    d1 = DeviceInputs(x)
+    h = _handle(api, x, 4)
+    o1, l1 = (t.clone() for t in d1.run(h, 4))
+    perm = np.random.default_rng(33).permutation(x.num_slots)
+    y = I.VerifyInputs(q=x.q, kv_rows=x.kv_rows, slot_idx=perm[x.slot_idx].astype(np.int32),
+                       seq_lens=x.seq_lens, q_lens=x.q_lens, num_slots=x.num_slots, heads=x.heads)
+    d2 = DeviceInputs(y)
+    o2, l2 = d2.run(h, 4)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_request_alone_equals_request_in_batch(api):
+    x = I.make_custom(np.random.default_rng(34), [500, 1200, 90], [4, 16, 2], 8, 4000)
+    d = DeviceInputs(x)
+    out, lse = d.run(_handle(api, x, 6, max_q=16), 6)
+    torch.cuda.synchronize()
+    # request 1 alone, same slots and values
+    y = I.VerifyInputs(q=x.q[4:20], kv_rows=x.kv_rows[500:1700], slot_idx=x.slot_idx[500:1700],
+                       seq_lens=x.seq_lens[1:2], q_lens=x.q_lens[1:2], num_slots=x.num_slots, heads=8)
+    e = DeviceInputs(y)
+    o1, l1 = e.run(_handle(api, y, 6, max_q=16), 6)
+    torch.cuda.synchronize()
+    assert torch.equal(out[4:20], o1) and torch.equal(lse[4:20], l1)
+
+
+def test_overflow_fallback_rows(api):
+    """A key far above a row's first-block max sends the row through the exact fallback kernel."""
+    x = I.make_custom(np.random.default_rng(35), [2000], [4], 8, 4000)
+    q0 = oracle.bf16_bits_to_f64(x.q[0, 3])
+    # key 1500 aligned with (token 0, head 3): score ~ 1.6*|q|^2/sqrt(192) ~ 70 nats ~ 100 log2 units
+    x.kv_rows[1500] = I.f32_to_bf16_bits((1.6 * q0).astype(np.float32))
+    _check(api, x, 2, "overflow")
+    _check(api, x, 1, "overflow")
+
+
+def test_merge_kernel_alone(api):
+    x = I.make_custom(np.random.default_rng(36), [400, 37], [5, 3], 6, 1000)
+    S = 6
+    ref_o, ref_l, o_part, l_part = oracle.verify_attention_split(
+        x.q, x.pool(), x.slot_idx, x.seq_lens, x.q_lens, x.scale, S, return_partials=True)
+    B, H, maxq = 2, 6, 5
+    rows = maxq * H
+    op = np.zeros((B, S, rows, 512), np.float32)
+    lp = np.full((B, S, rows), -np.inf, np.float32)
+    tok = 0
+    for b, Q in enumerate(x.q_lens.tolist()):
+        for t in range(Q):
+            for h in range(H):
+                op[b, :, t * H + h] = o_part[tok + t, h]
+                lp[b, :, t * H + h] = l_part[tok + t, h]
+        tok += Q
+    dev = "cuda"
+    out = torch.empty((8, H, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((8, H), dtype=torch.float32, device=dev)
+    api.merge(torch.from_numpy(op).to(dev), torch.from_numpy(lp).to(dev), torch.from_numpy(x.q_lens).to(dev), out, lse)
+    torch.cuda.synchronize()
+    eo, el = max_errors(out, lse, ref_o, ref_l)
+    assert eo <= OUT_TOL and el <= LSE_TOL
+
+
+def test_stale_workspace_is_not_read(api):
+    """A call with more splits, then one with fewer and shorter requests, on one handle."""
+    x = I.make_custom(np.random.default_rng(37), [5000], [16], 16, 12000)
+    y = I.make_custom(np.random.default_rng(38), [700], [16], 16, 12000)
+    h = _handle(api, x, 32)
+    DeviceInputs(x).run(h, 32)
+    dy = DeviceInputs(y)
+    out, lse = dy.run(h, 3)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle.verify_attention(y.q, y.pool(), y.slot_idx, y.seq_lens, y.q_lens, y.scale)
+    eo, el = max_errors(out, lse, ref_o, ref_l)
+    assert eo <= OUT_TOL and el <= LSE_TOL
+
+
+def test_graph_replay_matches_eager(api):
+    x = I.make_custom(np.random.default_rng(39), [3000, 1000], [16, 16], 16, 8000)
+    d = DeviceInputs(x)
+    h = _handle(api, x, 8)
+    out_e, lse_e = (t.clone() for t in d.run(h, 8))
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        d.run(h, 8)  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        d.run(h, 8)
+    for i in range(4):
+        d.out.fill_(0)
+        d.lse.fill_(0)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(d.out, out_e) and torch.equal(d.lse, lse_e), f"replay {i}"
+        # eager work between replays
+        d.run(h, 8)
+        torch.cuda.synchronize()
+
+
+def test_run_to_run_bitwise(api):
+    x = I.make_inputs("ctx4k")
+    d = DeviceInputs(x)
+    h = _handle(api, x, 8)
+    o1, l1 = (t.clone() for t in d.run(h, 8))
+    o2, l2 = d.run(h, 8)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_error_codes(api):
+    from speculative_decode_mla_amd import _lib
+    x = I.make_custom(np.random.default_rng(40), [100], [4], 4, 200)
+    d = DeviceInputs(x)
+    h = _handle(api, x, 4)
+    with pytest.raises(_lib.MlaVerifyError) as e:
+        d.run(h, 5)
+    assert e.value.status == _lib.MLA_ERR_INVALID_ARGUMENT
+    with pytest.raises(_lib.MlaVerifyError) as e:
+        d.run(h, 0)
+    assert e.value.status == _lib.MLA_ERR_INVALID_ARGUMENT
+    lib = _lib.load()
+    import ctypes
+    misaligned = ctypes.c_void_p(d.q.data_ptr() + 2)
+    st = lib.mla_verify_run(h._h, misaligned, ctypes.c_void_p(d.pool.data_ptr()), ctypes.c_void_p(d.slot_idx.data_ptr()),
+                            ctypes.c_void_p(d.seq_lens.data_ptr()), ctypes.c_void_p(d.q_lens.data_ptr()),
+                            ctypes.c_void_p(d.out.data_ptr()), ctypes.c_void_p(d.lse.data_ptr()), 1, None)
+    assert st == _lib.MLA_ERR_INVALID_ARGUMENT
