@@ -19,9 +19,9 @@ struct mla_verify_s {
 
 namespace {
 
-// Splits are given at least this many 64-key tiles, so a short request does not
+// Splits are given at least this many 32-key tiles, so a short request does not
 // fan out into many tiny partials (the result does not depend on the split count).
-constexpr int32_t kMinTilesPerSplit = 4;
+constexpr int32_t kMinTilesPerSplit = 8;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 

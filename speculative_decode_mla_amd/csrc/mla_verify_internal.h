@@ -13,7 +13,7 @@ constexpr int kRowBytes = kDqk * 2;  // one bf16 latent row: 1152 B = 9 x 128-B 
 constexpr int kWaves = 4;            // waves per workgroup (one per SIMD)
 constexpr int kRowsPerWave = 32;     // (token, head) rows owned by one wave
 constexpr int kRowsPerGroup = kWaves * kRowsPerWave;  // rows per workgroup: 128
-constexpr int kTileKeys = 64;        // keys gathered into LDS per step
+constexpr int kTileKeys = 32;        // keys gathered into LDS per step (one MFMA block)
 
 // Kernel 1: one workgroup per (request, split, 128-row group).
 struct PartialArgs {

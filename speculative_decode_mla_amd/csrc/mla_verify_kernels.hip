@@ -9,30 +9,31 @@
 // "The Context" and "What This Reveals About the Bottleneck", laid out for
 // CDNA4 rather than for the sm_120 part the page targets.
 //
-// Kernel 1 data flow (one workgroup = 4 waves, one per SIMD):
-//   * Gather: 64 keys per step.  Each key's 1152-B latent row (9 whole 128-B
-//     lines) is fetched through slot_idx straight into LDS with 16-B
-//     direct-to-LDS loads, 8 lanes per 128-B line.  Two LDS buffers: the
-//     next step's rows stream in while the current step computes.
-//   * LDS tile layout: key k, 16-B chunk c of its row lives at
-//       ((k/8)*9 + c/8)*1024 + (k%8)*128 + ((c%8) ^ (k%8))*16
+// Kernel 1, one workgroup = 4 waves (one per SIMD), 32 (token, head) rows per wave:
+//   * Slot staging: the split's slot indices (up to 4096 at a time) are copied
+//     to LDS once, so the gather never waits on a global index load.
+//   * Gather: 32 keys per tile.  Each key's 1152-B latent row (9 whole 128-B
+//     lines) goes straight from HBM into LDS with 16-B direct-to-LDS loads,
+//     8 lanes per 128-B line.  A ring of 4 tile buffers; the load of tile i+3
+//     is issued while tile i is being consumed.
+//   * LDS tile layout: key k (0..31), 16-B chunk c (0..71) of its row lives at
+//       ((k/8)*9 + c/8)*1024 + (k%8)*128 + ((c%8) ^ f(k))*16,  f(k) = (k%8) ^ ((k/8)%2)
 //     so one load instruction fills one 1 KiB block (8 keys x 128 B), and the
-//     XOR makes both the row reads for Q.K and the transposed reads for P.V
-//     hit distinct banks.
+//     XOR spreads both read patterns below over all banks.
 //   * Q.K on MFMA 32x32x16 bf16 as S^T = K . Q^T: K (32 keys x 16 dims) is the
 //     A operand read from LDS, the wave's 32 query rows are the B operand held
-//     in registers for the whole split (36 fragments cover 576 dims).  The
-//     C layout then gives each lane one row and 16 keys, so the softmax row
-//     statistics need one cross-lane step (lane l and l^32 share a row).
-//   * Online softmax in base 2 with the scale folded in; the running max is
-//     only raised when a row's max grows by more than 2^8, so the rescale of
-//     the 256 accumulator registers is rare.  Causal mask only on steps that
-//     reach the draft block (keys >= L - Q + 1).
+//     in registers for the whole split (36 fragments cover 576 dims).  In the C
+//     layout each lane then holds one row and 16 keys; lanes l and l^32 share a
+//     row.
+//   * Softmax in base 2 with the scale folded in, against a per-row reference
+//     max fixed at the split's first tile with a visible key; the exponentials
+//     of tile i are computed while the MFMA unit runs Q.K of tile i+1.  Causal
+//     mask on the draft block (keys >= L - Q + 1).
 //   * P.V as O^T = V^T . P^T: the probabilities stay in registers as the B
-//     operand (the S^T C layout is already a valid B layout after a fixed
-//     permutation of the key order, which the V^T operand repeats), and V^T
-//     fragments come from LDS with ds_read_b64_tr_b16, which transposes 4x16
-//     blocks of bf16 across each 16-lane group.
+//     operand (the S^T C layout is a valid B layout after a fixed permutation
+//     of the key order, which the V^T operand repeats), and V^T fragments come
+//     from LDS with ds_read_b64_tr_b16, which transposes 4x16 blocks of bf16
+//     across each 16-lane group.
 #include "mla_verify_internal.h"
 
 namespace mlav {
@@ -46,14 +47,21 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) char lds_char;
 
-constexpr int kTileBytes = kTileKeys * kRowBytes;         // 73,728 B per LDS buffer
-constexpr int kBlockBytes = 1024;                         // one direct-to-LDS instruction
-constexpr int kKeyBlockBytes = 9 * kBlockBytes;           // 8 keys x 1152 B
-constexpr int kKeyBlocksPerWave = kTileKeys / 8 / kWaves; // 2: key blocks each wave gathers
-constexpr int kQkSteps = kDqk / 16;                       // 36 MFMA k-steps over 576 dims
-constexpr int kColBlocks = kDv / 32;                      // 16 blocks of 32 output columns
-constexpr int kPrefetch = 6;                              // LDS fragment reads in flight ahead of the MFMA
+constexpr int kTileBytes = kTileKeys * kRowBytes;  // 36,864 B per LDS tile buffer
+constexpr int kRing = 4;                           // tile buffers
+constexpr int kAhead = kRing - 1;                  // tiles in flight ahead of the one being consumed
+constexpr int kChunkKeys = 4096;                   // slot indices staged in LDS at a time
+constexpr int kSlotBytes = kChunkKeys * 4;
+constexpr int kBlockBytes = 1024;                  // one direct-to-LDS instruction: 8 keys x 128 B
+constexpr int kKeyBlockBytes = 9 * kBlockBytes;    // 8 keys x 1152 B
+constexpr int kQkSteps = kDqk / 16;                // 36 MFMA k-steps over 576 dims
+constexpr int kColBlocks = kDv / 32;               // 16 blocks of 32 output columns
+constexpr int kPvSteps = 2 * kColBlocks;           // 32 MFMAs of P.V per tile
+constexpr int kPrefetch = 6;                       // LDS fragment reads kept ahead of their MFMA
+constexpr int kDmaPerTile = 9;                     // direct-to-LDS loads per wave per tile
 constexpr float kLn2 = 0.69314718055994530942f;
+static_assert(kTileKeys == 32 && kWaves * 8 == kTileKeys, "one 8-key block per wave per tile");
+static_assert(kRing * kTileBytes + kSlotBytes <= 163840, "LDS budget");
 
 // Number of splits that carry keys for a request of L keys; both kernels use it.
 __device__ __forceinline__ int split_count(int L, int nsplit, int min_tiles) {
@@ -80,13 +88,23 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// max / sum of v over lanes l and l^32 (the two lanes that hold one row)
+__device__ __forceinline__ float pair_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // MFMA 32x32x16 bf16 issued through inline asm so that the accumulator stays in
 // the register class chosen here: the 256-register output accumulator in
-// AGPRs, the per-block scores in VGPRs.  The compiler does not look inside
+// AGPRs, the per-tile scores in VGPRs.  The compiler does not look inside
 // these statements, so the wait states it would otherwise insert are given
 // explicitly: "s_nop 2" ahead of each MFMA covers a VALU write of an operand
-// register just before it, and the s_nop blocks below cover an MFMA result
-// read by VALU code.
+// register just before it, and MLAV_MFMA_DRAIN covers an MFMA result read by
+// VALU code.
 __device__ __forceinline__ void mfma_acc_a(f32x16& acc, const bf16x8& a, const bf16x8& b) {
   asm("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
@@ -116,6 +134,9 @@ __device__ __forceinline__ void dma16(const void* gsrc, uint32_t lds_addr) {
                : "memory", "m0");
 }
 #pragma clang diagnostic pop
+
+// s_waitcnt vmcnt(n) with lgkmcnt/expcnt left alone (gfx9 encoding; n < 16).
+#define MLAV_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (0x7 << 4) | (0xF << 8))
 
 // bf16 bits -> fp32
 __device__ __forceinline__ float bf16f(uint16_t b) { return __builtin_bit_cast(float, (uint32_t)b << 16); }
@@ -205,21 +226,106 @@ __device__ __forceinline__ void redo_rows_exact(const PartialArgs& p, const Work
   }
 }
 
-}  // namespace
+// Per-row softmax state of one lane (row lrow; the lane pair l, l^32 agrees on
+// every field but the two partial sums).
+struct RowSoftmax {
+  float m_ref;    // reference max (log2 units), -inf until a visible key is seen
+  float l_run;    // this lane's share of the row sum of bf16-rounded P (normalises O)
+  float l_exact;  // ... and of P before rounding (gives the LSE)
+  bool overflow;  // a score exceeded m_ref + kRefHeadroom: redo the row exactly
+  float mref;     // m_ref, or 0 while it is -inf (then every P is 0)
+};
 
 // Headroom (log2 units) above a row's reference max before exp2 could overflow
 // the fp32 sums: p = 2^(x - m_ref) <= 2^64, times <= 2^31 keys, stays finite.
 constexpr float kRefHeadroom = 64.0f;
 
+// Softmax of one tile, cut into kSoftmaxSlots slices that are placed between the
+// Q.K MFMAs of the next tile (one slice per MFMA).  Each slice issues only a few
+// VALU ops that do not depend on one another, so the in-order issue of the wave
+// never waits long on a VALU result while the MFMA unit is busy:
+//   0..3   scale 4 scores each                  4..7  row max (max3 tree, lane pair)
+//   8      reference max update                 9..27 software-pipelined per score j:
+//          slot 9+j: x - m_ref   slot 10+j: exp2   slot 11+j: bf16 pack, exact sum
+//          slot 12+j: rounded sum.
+// The causal mask is applied to the raw scores beforehand, on the tiles that
+// reach the draft block only.
+constexpr int kSoftmaxSlots = 28;
+struct SoftmaxTile {
+  f32x16 s;       // scores -> scaled -> x - mref -> exp2
+  float m[7];     // max tree
+  i32x4 pk[2];    // bf16 pairs (MFMA B operand for the two 16-key steps)
+};
+
+__device__ __forceinline__ void softmax_slot(int slot, SoftmaxTile& t, RowSoftmax& st, float scale_log2) {
+  if (slot < 4) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) t.s[4 * slot + u] *= scale_log2;
+    return;
+  }
+  if (slot == 4) {
+#pragma unroll
+    for (int u = 0; u < 5; ++u) t.m[u] = fmaxf(fmaxf(t.s[3 * u], t.s[3 * u + 1]), t.s[3 * u + 2]);
+    return;
+  }
+  if (slot == 5) {
+    t.m[5] = fmaxf(fmaxf(t.m[0], t.m[1]), t.m[2]);
+    t.m[6] = fmaxf(fmaxf(t.m[3], t.m[4]), t.s[15]);
+    return;
+  }
+  if (slot == 6) {
+    t.m[0] = fmaxf(t.m[5], t.m[6]);
+    return;
+  }
+  if (slot == 7) {
+    t.m[0] = pair_max(t.m[0]);
+    return;
+  }
+  if (slot == 8) {
+    const float mx = t.m[0];
+    st.m_ref = (st.m_ref == -INFINITY) ? mx : st.m_ref;
+    st.overflow |= mx > st.m_ref + kRefHeadroom;
+    st.mref = (st.m_ref == -INFINITY) ? 0.f : st.m_ref;
+    return;
+  }
+  const int a = slot - 9, b = slot - 10, c = slot - 11, d = slot - 12;
+  if (a >= 0 && a < 16) t.s[a] -= st.mref;
+  if (b >= 0 && b < 16) t.s[b] = __builtin_amdgcn_exp2f(t.s[b]);
+  if (c >= 0 && c < 16) {
+    st.l_exact += t.s[c];
+    if (c & 1) {
+      typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+      const bf16x2 pr = {(__bf16)t.s[c - 1], (__bf16)t.s[c]};
+      t.pk[c >> 3][(c >> 1) & 3] = __builtin_bit_cast(int, pr);
+    }
+  }
+  if (d >= 0 && d < 16 && (d & 1)) {
+    const int pair = t.pk[d >> 3][(d >> 1) & 3];
+    st.l_run += __builtin_bit_cast(float, pair << 16) + __builtin_bit_cast(float, pair & (int)0xFFFF0000);
+  }
+}
+
+// Causal mask on the raw scores of a tile that reaches the draft block:
+// lane holds keys key0 + 8*(j>>2) + (j&3) (key0 includes 4*hi); keys >= limit get -inf.
+__device__ __forceinline__ void mask_tile(f32x16& s, int key0, int limit) {
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int key = key0 + 8 * (j >> 2) + (j & 3);
+    s[j] = key < limit ? s[j] : -INFINITY;
+  }
+}
+
+}  // namespace
+
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void mla_verify_partial(PartialArgs p) {
-  __shared__ __attribute__((aligned(1024))) char smem_raw[2 * kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char smem_raw[kRing * kTileBytes + kSlotBytes];
   lds_char* smem = (lds_char*)smem_raw;
+  int32_t* slot_lds = (int32_t*)(smem_raw + kRing * kTileBytes);
 
   WorkItem wi;
   if (!decode_work(p, blockIdx.x, wi)) return;
   const int L = wi.L, Q = wi.Q, H = p.heads, R = wi.R;
-  const int t_begin = wi.t_begin, t_end = wi.t_end;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int hi = lane >> 5, lrow = lane & 31;
@@ -227,36 +333,20 @@ void mla_verify_partial(PartialArgs p) {
   const bool row_valid = myrow < R;
   const int tok = row_valid ? myrow / H : 0;
   const int limit = L - Q + tok + 1;  // this row sees keys [0, limit)
-  const int mask_from = L - Q + 1;    // first key that some draft row cannot see
+  const int mask_from = L - Q + 1;    // first key some draft row cannot see
 
-  // ---- gather set-up --------------------------------------------------------------------------
-  const int g_kr = lane >> 3;                   // key within an 8-key block
-  const int g_byte = ((lane & 7) ^ g_kr) << 4;  // 16-B chunk of the 128-B line this lane moves
-  const int32_t* slots = p.slot_idx + wi.ko;
+  // ---- gather set-up: wave w moves keys 8w..8w+7 of every tile --------------------------------
+  const int g_kr = lane >> 3;                             // key within the wave's 8-key block
+  const int g_byte = ((lane & 7) ^ g_kr ^ (w & 1)) << 4;  // 16-B chunk of the 128-B line
   const char* kv = (const char*)p.kv;
-  auto slot_of = [&](int tile, int e) {
-    int key = tile * kTileKeys + (w * kKeyBlocksPerWave + e) * 8 + g_kr;
-    key = key < L ? key : L - 1;  // ragged tail: repeat the last row (masked out below)
-    return slots[key];
-  };
   const uint32_t smem_base = (uint32_t)(uintptr_t)smem;
   const int w_uniform = __builtin_amdgcn_readfirstlane(w);
-  auto issue_tile = [&](int buf, int sl0, int sl1) {
-    const uint32_t base = smem_base + buf * kTileBytes + w_uniform * kKeyBlocksPerWave * kKeyBlockBytes;
-    const char* r0 = kv + (int64_t)sl0 * kRowBytes + g_byte;
-    const char* r1 = kv + (int64_t)sl1 * kRowBytes + g_byte;
+  auto issue_tile = [&](int buf, int slot) {
+    const uint32_t base = smem_base + buf * kTileBytes + w_uniform * kKeyBlockBytes;
+    const char* row = kv + (int64_t)slot * kRowBytes + g_byte;
 #pragma unroll
-    for (int cg = 0; cg < 9; ++cg) dma16(r0 + cg * 128, base + cg * kBlockBytes);
-#pragma unroll
-    for (int cg = 0; cg < 9; ++cg) dma16(r1 + cg * 128, base + kKeyBlockBytes + cg * kBlockBytes);
+    for (int cg = 0; cg < kDmaPerTile; ++cg) dma16(row + cg * 128, base + cg * kBlockBytes);
   };
-
-  int sl0 = slot_of(t_begin, 0), sl1 = slot_of(t_begin, 1);
-  issue_tile(0, sl0, sl1);
-  if (t_begin + 1 < t_end) {
-    sl0 = slot_of(t_begin + 1, 0);
-    sl1 = slot_of(t_begin + 1, 1);
-  }
 
   // ---- the wave's 32 query rows, resident for the whole split ----------------------------------
   // lane holds row lrow, dims 16*ks + 8*hi .. +7 (MFMA B-operand layout)
@@ -268,126 +358,142 @@ void mla_verify_partial(PartialArgs p) {
     for (int ks = 0; ks < kQkSteps; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, qrow[2 * ks] & keep);
   }
 
-  // ---- per-lane LDS read addresses -----------------------------------------------------------
-  // Q.K A operand: lane reads key (kb*32 + lrow), 16-B chunk (2*ks + hi).
+  // ---- per-lane LDS read addresses (relative to a tile buffer) ---------------------------------
+  // Q.K A operand: lane reads key lrow, 16-B chunk 2*ks + hi.
   int kaddr[4];
   {
-    const int base = (lrow >> 3) * kKeyBlockBytes + (lrow & 7) * 128;
-    const int y = hi ^ (lrow & 7);
+    const int kr = lrow & 7, f = kr ^ ((lrow >> 3) & 1);
+    const int base = (lrow >> 3) * kKeyBlockBytes + kr * 128;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) kaddr[j] = base + (((2 * j) ^ y) << 4);
+    for (int j = 0; j < 4; ++j) kaddr[j] = base + (((2 * j) ^ hi ^ f) << 4);
   }
-  // P.V A operand via the 4x16 transposing read: in 16-lane group G, lane j reads
-  // key 4*(G>>1) + (j>>2) (+ 16*kk + 8*r) at columns 32*cb + 16*(G&1) + 4*(j&3) .. +3;
-  // lane l then holds column 32*cb + (l&31) for keys 16*kk + 8*r + 4*(l>>5) .. +3.
-  int vaddr[2];
+  // P.V A operand via the 4x16 transposing read: in 16-lane group G, lane j reads key
+  // 16*kk + 8*r + 4*(G>>1) + (j>>2) at columns 32*cb + 16*(G&1) + 4*(j&3) .. +3; lane l then
+  // holds column 32*cb + (l&31) for keys 16*kk + 8*r + 4*(l>>5) .. +3.
+  int vaddr[2][2];
   {
     const int G = lane >> 4, j = lane & 15;
     const int kr = 4 * (G >> 1) + (j >> 2);
-    const int z = (2 * (G & 1) + ((j & 3) >> 1)) ^ kr;
+    const int u = 2 * (G & 1) + ((j & 3) >> 1);
 #pragma unroll
-    for (int e = 0; e < 2; ++e) vaddr[e] = kr * 128 + (((4 * e) ^ z) << 4) + (j & 1) * 8;
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+        vaddr[e][r] = r * kKeyBlockBytes + kr * 128 + (((4 * e) ^ u ^ kr ^ r) << 4) + (j & 1) * 8;
   }
 
   f32x16 o[kColBlocks];
 #pragma unroll
   for (int cb = 0; cb < kColBlocks; ++cb) o[cb] = (f32x16){};
   // Softmax with a fixed per-row reference: m_ref is the row max of the split's
-  // first block with a visible key; p = 2^(x - m_ref) is exact as long as no
+  // first tile with a visible key; p = 2^(x - m_ref) is exact as long as no
   // later score exceeds m_ref by more than kRefHeadroom.  A row that does is
   // recomputed exactly at the end (redo_rows_exact).
-  float m_ref = -INFINITY;
-  float l_run = 0.f;    // this lane's share of the row sum of bf16-rounded P
-  float l_exact = 0.f;  // ... and of P before rounding
-  bool overflow = false;
+  RowSoftmax st{-INFINITY, 0.f, 0.f, false, 0.f};
 
-  for (int it = t_begin; it < t_end; ++it) {
-    const int buf = (it - t_begin) & 1;
-    __builtin_amdgcn_s_waitcnt(0x0070 /* vmcnt(0) lgkmcnt(0) */);
-    __syncthreads();
-    if (it + 1 < t_end) {
-      issue_tile(buf ^ 1, sl0, sl1);
-      if (it + 2 < t_end) {
-        sl0 = slot_of(it + 2, 0);
-        sl1 = slot_of(it + 2, 1);
-      }
+  const int32_t* slots_g = p.slot_idx + wi.ko;
+  for (int c0 = wi.t_begin; c0 < wi.t_end; c0 += kChunkKeys / kTileKeys) {
+    const int c1 = min(wi.t_end, c0 + kChunkKeys / kTileKeys);  // tiles [c0, c1) in this chunk
+    const int ntiles = c1 - c0;
+    // stage the chunk's slot indices (ragged tail: repeat the last key, masked out below)
+    __syncthreads();  // the previous chunk is fully consumed
+    for (int i = tid; i < ntiles * kTileKeys; i += kWaves * 64) {
+      const int key = min(c0 * kTileKeys + i, L - 1);
+      slot_lds[i] = slots_g[key];
     }
-    const lds_char* tb = smem + buf * kTileBytes;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {  // two 32-key blocks per tile
-      const int k0 = it * kTileKeys + kb * 32;
-      const lds_char* kbp = tb + kb * 4 * kKeyBlockBytes;
+    __syncthreads();
+    auto slot_of = [&](int t) { return slot_lds[(t - c0) * kTileKeys + w * 8 + g_kr]; };
+    const int nfirst = min(ntiles, kAhead);
+    for (int t = 0; t < nfirst; ++t) issue_tile(t, slot_of(c0 + t));
+    int slot_next = ntiles > kAhead ? slot_of(c0 + kAhead) : 0;
 
-      // S^T = K . Q^T: 32 keys x the wave's 32 rows.  K fragments are read
-      // kPrefetch steps ahead of the MFMA that consumes them; the scheduling
-      // barriers keep the compiler from sinking the reads next to their use.
-      bf16x8 kf[kQkSteps];
-      auto kread = [&](int ks) {
-        kf[ks] = *(const __attribute__((address_space(3))) bf16x8*)(kbp + kaddr[ks & 3] + (ks >> 2) * kBlockBytes);
-      };
+    // tile c0 must be complete before its Q.K
+    if (nfirst == 3) MLAV_WAIT_VMCNT(2 * kDmaPerTile);
+    else if (nfirst == 2) MLAV_WAIT_VMCNT(kDmaPerTile);
+    else MLAV_WAIT_VMCNT(0);
+    __syncthreads();
+
+    bf16x8 kf[kQkSteps];
+    auto kread = [&](const lds_char* tb, int ks) {
+      kf[ks] = *(const __attribute__((address_space(3))) bf16x8*)(tb + kaddr[ks & 3] + (ks >> 2) * kBlockBytes);
+    };
+    f32x16 sacc;
+    {
+      const lds_char* tb = smem;
 #pragma unroll
-      for (int ks = 0; ks < kPrefetch; ++ks) kread(ks);
-      f32x16 sacc;
+      for (int ks = 0; ks < kPrefetch; ++ks) kread(tb, ks);
 #pragma unroll
       for (int ks = 0; ks < kQkSteps; ++ks) {
         __builtin_amdgcn_sched_barrier(0);
-        if (ks + kPrefetch < kQkSteps) kread(ks + kPrefetch);
+        if (ks + kPrefetch < kQkSteps) kread(tb, ks + kPrefetch);
         __builtin_amdgcn_sched_barrier(0);
         if (ks == 0) mfma_first_v(sacc, kf[ks], qf[ks]);
         else mfma_acc_v(sacc, kf[ks], qf[ks]);
       }
       __builtin_amdgcn_sched_barrier(0);
+    }
+
+    for (int i = 0; i < ntiles; ++i) {
+      const int t = c0 + i;
+      const lds_char* tb = smem + (i & (kRing - 1)) * kTileBytes;
+      const int key0 = t * kTileKeys + 4 * hi;
       asm volatile(MLAV_MFMA_DRAIN : "+v"(sacc));
-
-      // softmax numerators (base 2): lane holds row lrow, keys k0 + 8*(j>>2) + 4*hi + (j&3)
-      sacc *= p.scale_log2;
-      if (k0 + 32 > mask_from) {
+      SoftmaxTile sm;
+      sm.s = sacc;
+      if (t * kTileKeys + kTileKeys > mask_from) mask_tile(sm.s, key0, limit);
+      if (i + 1 < ntiles) {
+        // tile i+1 complete (its loads are the oldest still counted), then publish it
+        if (i + 2 < ntiles) MLAV_WAIT_VMCNT(kDmaPerTile);
+        else MLAV_WAIT_VMCNT(0);
+        __syncthreads();
+        const bool refill = i + kAhead < ntiles;
+        const uint32_t dma_base = smem_base + ((i + kAhead) & (kRing - 1)) * kTileBytes + w_uniform * kKeyBlockBytes;
+        const char* dma_row = kv + (int64_t)slot_next * kRowBytes + g_byte;
+        // Q.K of tile i+1; between its MFMAs: the softmax of tile i and the
+        // loads that refill the ring with tile i+kAhead
+        const lds_char* nb = smem + ((i + 1) & (kRing - 1)) * kTileBytes;
+        f32x16 snext;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int key = k0 + 8 * (j >> 2) + 4 * hi + (j & 3);
-          sacc[j] = key < limit ? sacc[j] : -INFINITY;
+        for (int ks = 0; ks < kPrefetch; ++ks) kread(nb, ks);
+#pragma unroll
+        for (int ks = 0; ks < kQkSteps; ++ks) {
+          __builtin_amdgcn_sched_barrier(0);
+          if (ks + kPrefetch < kQkSteps) kread(nb, ks + kPrefetch);
+          __builtin_amdgcn_sched_barrier(0);
+          if (ks == 0) mfma_first_v(snext, kf[ks], qf[ks]);
+          else mfma_acc_v(snext, kf[ks], qf[ks]);
+          __builtin_amdgcn_sched_barrier(0);
+          if (ks < kSoftmaxSlots) softmax_slot(ks, sm, st, p.scale_log2);
+          if (ks >= 1 && ks <= kDmaPerTile && refill) dma16(dma_row + (ks - 1) * 128, dma_base + (ks - 1) * kBlockBytes);
+          if (ks == kDmaPerTile + 1 && i + kAhead + 1 < ntiles) slot_next = slot_of(t + kAhead + 1);
         }
+        __builtin_amdgcn_sched_barrier(0);
+        sacc = snext;
+      } else {
+#pragma unroll
+        for (int slot = 0; slot < kSoftmaxSlots; ++slot) softmax_slot(slot, sm, st, p.scale_log2);
       }
-      float mx = sacc[0];
-#pragma unroll
-      for (int j = 1; j < 16; ++j) mx = fmaxf(mx, sacc[j]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      m_ref = (m_ref == -INFINITY) ? mx : m_ref;
-      overflow |= mx > m_ref + kRefHeadroom;
-      const float mref = (m_ref == -INFINITY) ? 0.f : m_ref;
-      // P is rounded to bf16 for the MFMA.  Two row sums: of the rounded values,
-      // which normalises O (so o_s is a convex combination of the weights the
-      // MFMA actually used), and of the unrounded values, which gives the LSE.
-      bf16x8 pf[2];
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float pv = __builtin_amdgcn_exp2f(sacc[kk * 8 + i] - mref);
-          const __bf16 pb = (__bf16)pv;
-          pf[kk][i] = pb;
-          l_run += (float)pb;
-          l_exact += pv;
-        }
+      bf16x8 pf[2] = {__builtin_bit_cast(bf16x8, sm.pk[0]), __builtin_bit_cast(bf16x8, sm.pk[1])};
 
-      // O^T += V^T . P^T over these 32 keys; V^T fragments read kPrefetch ahead
-      bf16x8 vf[2 * kColBlocks];
-      auto vread = [&](int i) {  // fragment i = (column block i/2, 16-key step i%2)
-        const int cb = i >> 1, kk = i & 1;
-        const lds_char* vb = tb + vaddr[cb & 1] + (cb >> 1) * kBlockBytes + (kb * 4 + 2 * kk) * kKeyBlockBytes;
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)vb);
+      // O^T += V^T . P^T over tile i (fragment n: column block n%16, 16-key step n/16)
+      bf16x8 vf[kPvSteps];
+      auto vread = [&](int n) {
+        const int cb = n & (kColBlocks - 1), kk = n >> 4;
+        const lds_char* vb = tb + (cb >> 1) * kBlockBytes + kk * 2 * kKeyBlockBytes;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(vb + vaddr[cb & 1][0]));
         const i16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4*)(vb + kKeyBlockBytes));
-        vf[i] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
+            (__attribute__((address_space(3))) i16x4*)(vb + vaddr[cb & 1][1]));
+        vf[n] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
       };
 #pragma unroll
-      for (int i = 0; i < kPrefetch; ++i) vread(i);
+      for (int n = 0; n < kPrefetch; ++n) vread(n);
 #pragma unroll
-      for (int i = 0; i < 2 * kColBlocks; ++i) {
+      for (int n = 0; n < kPvSteps; ++n) {
         __builtin_amdgcn_sched_barrier(0);
-        if (i + kPrefetch < 2 * kColBlocks) vread(i + kPrefetch);
+        if (n + kPrefetch < kPvSteps) vread(n + kPrefetch);
         __builtin_amdgcn_sched_barrier(0);
-        mfma_acc_a(o[i >> 1], vf[i], pf[i & 1]);
+        mfma_acc_a(o[n & (kColBlocks - 1)], vf[n], pf[n >> 4]);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -396,8 +502,8 @@ void mla_verify_partial(PartialArgs p) {
 
   // ---- partial write: o_s = O / l, lse_s = ln2 * (m_ref + log2 l) -------------------------------
   if (!row_valid) return;
-  const float lt = l_run + __shfl_xor(l_run, 32);
-  const float le = l_exact + __shfl_xor(l_exact, 32);
+  const float lt = pair_sum(st.l_run);
+  const float le = pair_sum(st.l_exact);
   const float inv = lt > 0.f ? 1.0f / lt : 0.f;
   const int64_t prow = ((int64_t)wi.bs * p.rows_pad + myrow);
   float* dst = p.o_part + prow * kDv + 4 * hi;
@@ -408,10 +514,10 @@ void mla_verify_partial(PartialArgs p) {
       f32x4 v = {o[cb][4 * q4 + 0] * inv, o[cb][4 * q4 + 1] * inv, o[cb][4 * q4 + 2] * inv, o[cb][4 * q4 + 3] * inv};
       *(f32x4*)(dst + cb * 32 + 8 * q4) = v;
     }
-  if (hi == 0) p.lse_part[prow] = le > 0.f ? (m_ref + __builtin_amdgcn_logf(le)) * kLn2 : -INFINITY;
+  if (hi == 0) p.lse_part[prow] = le > 0.f ? (st.m_ref + __builtin_amdgcn_logf(le)) * kLn2 : -INFINITY;
 
   // Rows whose scores outgrew the fixed reference are redone exactly by the wave.
-  const uint64_t redo = __ballot(overflow && hi == 0);
+  const uint64_t redo = __ballot(st.overflow && hi == 0);
   if (redo != 0) redo_rows_exact(p, wi, wi.g * kRowsPerGroup + w * kRowsPerWave, (uint32_t)redo);
 }
 
