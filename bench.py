@@ -79,6 +79,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for the CPU baseline")
     ap.add_argument("--eager", action="store_true", help="plain launches, no graph (for profilers)")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="only run a plain 256 MiB device copy (reference size for HBM traffic counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
@@ -94,6 +96,15 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calib:
+        n = 256 << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "launches": 3}))
+        return
     w = I.WORKLOADS[args.workload]
     nsplit = args.nsplit or w.nsplit
     print(f"# workload {w.name}: B={w.batch} H={w.heads} Q={w.q_len} L={w.ctx or 'log-uniform'} "

@@ -50,18 +50,19 @@ typedef __attribute__((address_space(3))) char lds_char;
 constexpr int kTileBytes = kTileKeys * kRowBytes;  // 36,864 B per LDS tile buffer
 constexpr int kRing = 4;                           // tile buffers
 constexpr int kAhead = kRing - 1;                  // tiles in flight ahead of the one being consumed
-constexpr int kChunkKeys = 4096;                   // slot indices staged in LDS at a time
-constexpr int kSlotBytes = kChunkKeys * 4;
+constexpr int kXchgBytes = 2 * kWaves * 2048;      // bf16 P of every wave, two buffers
 constexpr int kBlockBytes = 1024;                  // one direct-to-LDS instruction: 8 keys x 128 B
 constexpr int kKeyBlockBytes = 9 * kBlockBytes;    // 8 keys x 1152 B
 constexpr int kQkSteps = kDqk / 16;                // 36 MFMA k-steps over 576 dims
 constexpr int kColBlocks = kDv / 32;               // 16 blocks of 32 output columns
-constexpr int kPvSteps = 2 * kColBlocks;           // 32 MFMAs of P.V per tile
-constexpr int kPrefetch = 6;                       // LDS fragment reads kept ahead of their MFMA
+constexpr int kHalfColBlocks = kColBlocks / 2;     // column blocks of one wave of a pair
+constexpr int kPvFrags = 2 * kHalfColBlocks;       // V^T fragments per wave per tile (2 MFMAs each)
+constexpr int kPrefetch = 6;                       // K fragment reads kept ahead of their MFMA
+constexpr int kVPrefetch = 4;                      // V^T fragment reads kept ahead
 constexpr int kDmaPerTile = 9;                     // direct-to-LDS loads per wave per tile
 constexpr float kLn2 = 0.69314718055994530942f;
 static_assert(kTileKeys == 32 && kWaves * 8 == kTileKeys, "one 8-key block per wave per tile");
-static_assert(kRing * kTileBytes + kSlotBytes <= 163840, "LDS budget");
+static_assert(kRing * kTileBytes + kXchgBytes <= 163840, "LDS budget");
 
 // Number of splits that carry keys for a request of L keys; both kernels use it.
 __device__ __forceinline__ int split_count(int L, int nsplit, int min_tiles) {
@@ -117,23 +118,41 @@ __device__ __forceinline__ void mfma_first_v(f32x16& acc, const bf16x8& a, const
 // 24 wait states: an MFMA result may now be read by VALU / accvgpr moves.
 #define MLAV_MFMA_DRAIN "s_nop 7\n\ts_nop 7\n\ts_nop 7"
 
-// 16-byte direct-to-LDS load: each lane moves 16 B from its global address to
-// LDS at lds_addr + 16*lane (lds_addr is wave-uniform, carried in M0).  Issued
-// through inline asm so the compiler does not fold these loads into its
-// lgkmcnt bookkeeping for the ds_read stream; their completion is awaited
-// explicitly (vmcnt) before the barrier that publishes a tile.  The s_nop is the
-// wait state required between writing M0 and an LDS-DMA instruction reading it.
-// M0 is a reserved register, hence the diagnostic push: nothing else in these
-// kernels uses M0 (no LDS-DMA builtins, no GDS, no s_sendmsg).
+// 16-byte direct-to-LDS load: each lane moves 16 B from gsrc + OFF to LDS at
+// m0 + OFF + 16*lane.  The immediate OFF applies to both addresses, so a caller
+// that wants the data at lds_addr passes m0 = lds_addr - OFF: the nine loads of a
+// key block then share one 64-bit row address and differ only in SALU-computed
+// M0 values and the immediate, with no VALU work per load.  Issued through inline
+// asm so the compiler does not fold these loads into its lgkmcnt bookkeeping for
+// the ds_read stream; their completion is awaited explicitly (vmcnt) before the
+// barrier that publishes a tile.  The s_nop is the wait state required between
+// writing M0 and an LDS-DMA instruction reading it.  M0 is a reserved register,
+// hence the diagnostic push: nothing else in these kernels uses M0 (no LDS-DMA
+// builtins, no GDS, no s_sendmsg).
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16(const void* gsrc, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+template <int OFF>
+__device__ __forceinline__ void dma16(const void* gsrc, uint32_t m0_value) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off offset:%2"
                :
-               : "v"(gsrc), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+               : "v"(gsrc), "s"(m0_value), "i"(OFF)
                : "memory", "m0");
 }
 #pragma clang diagnostic pop
+
+// One wave's share of a tile: key block w (8 keys x 1152 B) as nine 1 KiB loads;
+// load cg moves 16-B chunks [8cg, 8cg+8) of the eight rows (see the layout above).
+__device__ __forceinline__ void dma_key_block(const char* row, uint32_t lds_block) {
+  dma16<0 * 128>(row, lds_block + 0 * (kBlockBytes - 128));
+  dma16<1 * 128>(row, lds_block + 1 * (kBlockBytes - 128));
+  dma16<2 * 128>(row, lds_block + 2 * (kBlockBytes - 128));
+  dma16<3 * 128>(row, lds_block + 3 * (kBlockBytes - 128));
+  dma16<4 * 128>(row, lds_block + 4 * (kBlockBytes - 128));
+  dma16<5 * 128>(row, lds_block + 5 * (kBlockBytes - 128));
+  dma16<6 * 128>(row, lds_block + 6 * (kBlockBytes - 128));
+  dma16<7 * 128>(row, lds_block + 7 * (kBlockBytes - 128));
+  dma16<8 * 128>(row, lds_block + 8 * (kBlockBytes - 128));
+}
 
 // s_waitcnt vmcnt(n) with lgkmcnt/expcnt left alone (gfx9 encoding; n < 16).
 #define MLAV_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (0x7 << 4) | (0xF << 8))
@@ -233,7 +252,6 @@ struct RowSoftmax {
   float l_run;    // this lane's share of the row sum of bf16-rounded P (normalises O)
   float l_exact;  // ... and of P before rounding (gives the LSE)
   bool overflow;  // a score exceeded m_ref + kRefHeadroom: redo the row exactly
-  float mref;     // m_ref, or 0 while it is -inf (then every P is 0)
 };
 
 // Headroom (log2 units) above a row's reference max before exp2 could overflow
@@ -241,67 +259,67 @@ struct RowSoftmax {
 constexpr float kRefHeadroom = 64.0f;
 
 // Softmax of one tile, cut into kSoftmaxSlots slices that are placed between the
-// Q.K MFMAs of the next tile (one slice per MFMA).  Each slice issues only a few
-// VALU ops that do not depend on one another, so the in-order issue of the wave
-// never waits long on a VALU result while the MFMA unit is busy:
-//   0..3   scale 4 scores each                  4..7  row max (max3 tree, lane pair)
-//   8      reference max update                 9..27 software-pipelined per score j:
-//          slot 9+j: x - m_ref   slot 10+j: exp2   slot 11+j: bf16 pack, exact sum
-//          slot 12+j: rounded sum.
+// Q.K MFMAs of the next tile (one slice per MFMA).  A VALU op costs the wave 4
+// cycles (an exp 8) and only about 20 cycles of VALU fit under one 32-cycle MFMA,
+// so each slice is kept to a few independent ops:
+//   0..3  row max of the raw scores (max3 tree, lane pair), reference update
+//   4+j   x_j = s_j * scale - m_ref        (one FMA; the scale is folded in here)
+//   5+j   p_j = 2^x_j
+//   6+j   exact row sum; for odd j, bf16 pack of (p_{j-1}, p_j)
+//   7+j   for odd j, rounded row sum of the pair (v_dot2_f32_bf16 with (1, 1))
 // The causal mask is applied to the raw scores beforehand, on the tiles that
 // reach the draft block only.
-constexpr int kSoftmaxSlots = 28;
+constexpr int kSoftmaxSlots = 23;
 struct SoftmaxTile {
-  f32x16 s;       // scores -> scaled -> x - mref -> exp2
-  float m[7];     // max tree
-  i32x4 pk[2];    // bf16 pairs (MFMA B operand for the two 16-key steps)
+  f32x16 s;       // raw scores -> 2^(s*scale - m_ref)
+  float m[3];     // max tree
+  float nmref;    // -m_ref (0 while m_ref is -inf)
+  int pw[8];      // bf16 pairs; pw[0..3], pw[4..7] are the MFMA B operands of the two 16-key steps
+                  // (kept as separate scalars: element inserts into a vector here were miscompiled)
+  __device__ i32x4 operand(int kk) const { return (i32x4){pw[4 * kk], pw[4 * kk + 1], pw[4 * kk + 2], pw[4 * kk + 3]}; }
 };
 
 __device__ __forceinline__ void softmax_slot(int slot, SoftmaxTile& t, RowSoftmax& st, float scale_log2) {
-  if (slot < 4) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) t.s[4 * slot + u] *= scale_log2;
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  if (slot == 0) {
+    t.m[0] = fmaxf(fmaxf(t.s[0], t.s[1]), t.s[2]);
+    t.m[1] = fmaxf(fmaxf(t.s[3], t.s[4]), t.s[5]);
+    t.m[2] = fmaxf(fmaxf(t.s[6], t.s[7]), t.s[8]);
+    t.m[0] = fmaxf(fmaxf(t.m[0], t.s[9]), t.s[10]);
+    t.m[1] = fmaxf(fmaxf(t.m[1], t.s[11]), t.s[12]);
     return;
   }
-  if (slot == 4) {
-#pragma unroll
-    for (int u = 0; u < 5; ++u) t.m[u] = fmaxf(fmaxf(t.s[3 * u], t.s[3 * u + 1]), t.s[3 * u + 2]);
+  if (slot == 1) {
+    t.m[2] = fmaxf(fmaxf(t.m[2], t.s[13]), t.s[14]);
+    t.m[0] = fmaxf(fmaxf(t.m[0], t.m[1]), t.s[15]);
+    t.m[0] = fmaxf(t.m[0], t.m[2]);
     return;
   }
-  if (slot == 5) {
-    t.m[5] = fmaxf(fmaxf(t.m[0], t.m[1]), t.m[2]);
-    t.m[6] = fmaxf(fmaxf(t.m[3], t.m[4]), t.s[15]);
+  if (slot == 2) {
+    t.m[0] = pair_max(t.m[0]) * scale_log2;  // scale > 0 commutes with max
     return;
   }
-  if (slot == 6) {
-    t.m[0] = fmaxf(t.m[5], t.m[6]);
-    return;
-  }
-  if (slot == 7) {
-    t.m[0] = pair_max(t.m[0]);
-    return;
-  }
-  if (slot == 8) {
+  if (slot == 3) {
     const float mx = t.m[0];
     st.m_ref = (st.m_ref == -INFINITY) ? mx : st.m_ref;
     st.overflow |= mx > st.m_ref + kRefHeadroom;
-    st.mref = (st.m_ref == -INFINITY) ? 0.f : st.m_ref;
+    t.nmref = (st.m_ref == -INFINITY) ? 0.f : -st.m_ref;
     return;
   }
-  const int a = slot - 9, b = slot - 10, c = slot - 11, d = slot - 12;
-  if (a >= 0 && a < 16) t.s[a] -= st.mref;
+  const int a = slot - 4, b = slot - 5, c = slot - 6, d = slot - 7;
+  if (a >= 0 && a < 16) t.s[a] = __builtin_fmaf(t.s[a], scale_log2, t.nmref);
   if (b >= 0 && b < 16) t.s[b] = __builtin_amdgcn_exp2f(t.s[b]);
   if (c >= 0 && c < 16) {
     st.l_exact += t.s[c];
     if (c & 1) {
-      typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
       const bf16x2 pr = {(__bf16)t.s[c - 1], (__bf16)t.s[c]};
-      t.pk[c >> 3][(c >> 1) & 3] = __builtin_bit_cast(int, pr);
+      t.pw[c >> 1] = __builtin_bit_cast(int, pr);
     }
   }
   if (d >= 0 && d < 16 && (d & 1)) {
-    const int pair = t.pk[d >> 3][(d >> 1) & 3];
-    st.l_run += __builtin_bit_cast(float, pair << 16) + __builtin_bit_cast(float, pair & (int)0xFFFF0000);
+    const bf16x2 pr = __builtin_bit_cast(bf16x2, t.pw[d >> 1]);
+    const bf16x2 one = __builtin_bit_cast(bf16x2, 0x3f803f80);
+    st.l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, one, st.l_run, false);
   }
 }
 
@@ -319,17 +337,22 @@ __device__ __forceinline__ void mask_tile(f32x16& s, int key0, int limit) {
 
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void mla_verify_partial(PartialArgs p) {
-  __shared__ __attribute__((aligned(1024))) char smem_raw[kRing * kTileBytes + kSlotBytes];
+  __shared__ __attribute__((aligned(1024))) char smem_raw[kRing * kTileBytes + kXchgBytes];
   lds_char* smem = (lds_char*)smem_raw;
-  int32_t* slot_lds = (int32_t*)(smem_raw + kRing * kTileBytes);
+  lds_char* xchg = smem + kRing * kTileBytes;  // [2][kWaves][2 KiB]: bf16 P of each wave, double-buffered
 
   WorkItem wi;
   if (!decode_work(p, blockIdx.x, wi)) return;
   const int L = wi.L, Q = wi.Q, H = p.heads, R = wi.R;
+  const int ntiles = wi.t_end - wi.t_begin;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int hi = lane >> 5, lrow = lane & 31;
-  const int myrow = wi.g * kRowsPerGroup + w * kRowsPerWave + lrow;  // (token, head) row in the request
+  const int half = w & 1;   // this wave computes output columns [256*half, 256*half + 256)
+  const int partner = w ^ 1;
+  const int row0 = wi.g * kRowsPerGroup;
+  const int myrow = row0 + w * kRowsPerWave + lrow;        // own (token, head) row in the request
+  const int parrow = row0 + partner * kRowsPerWave + lrow; // the partner wave's row in this lane
   const bool row_valid = myrow < R;
   const int tok = row_valid ? myrow / H : 0;
   const int limit = L - Q + tok + 1;  // this row sees keys [0, limit)
@@ -341,12 +364,23 @@ void mla_verify_partial(PartialArgs p) {
   const char* kv = (const char*)p.kv;
   const uint32_t smem_base = (uint32_t)(uintptr_t)smem;
   const int w_uniform = __builtin_amdgcn_readfirstlane(w);
+  // Slot indices, 8 tiles per register: lane j holds the slot of key 8w + (j&7) of tile (base + j/8).
+  const int32_t* slots_g = p.slot_idx + wi.ko;
+  auto load_slots = [&](int first_tile) {
+    int key = (wi.t_begin + first_tile + (lane >> 3)) * kTileKeys + w * 8 + (lane & 7);
+    key = key < L ? key : L - 1;  // ragged tail / past the split: any valid row (masked out below)
+    return slots_g[key];
+  };
+  auto slot_for = [&](int sv, int i) { return __shfl(sv, 8 * (i & 7) + g_kr); };
   auto issue_tile = [&](int buf, int slot) {
     const uint32_t base = smem_base + buf * kTileBytes + w_uniform * kKeyBlockBytes;
-    const char* row = kv + (int64_t)slot * kRowBytes + g_byte;
-#pragma unroll
-    for (int cg = 0; cg < kDmaPerTile; ++cg) dma16(row + cg * 128, base + cg * kBlockBytes);
+    dma_key_block(kv + (int64_t)slot * kRowBytes + g_byte, base);
   };
+
+  int sv_cur = load_slots(0);
+  int sv_next = load_slots(8);
+  const int nfirst = min(ntiles, kAhead);
+  for (int i = 0; i < nfirst; ++i) issue_tile(i, slot_for(sv_cur, i));
 
   // ---- the wave's 32 query rows, resident for the whole split ----------------------------------
   // lane holds row lrow, dims 16*ks + 8*hi .. +7 (MFMA B-operand layout)
@@ -369,7 +403,8 @@ void mla_verify_partial(PartialArgs p) {
   }
   // P.V A operand via the 4x16 transposing read: in 16-lane group G, lane j reads key
   // 16*kk + 8*r + 4*(G>>1) + (j>>2) at columns 32*cb + 16*(G&1) + 4*(j&3) .. +3; lane l then
-  // holds column 32*cb + (l&31) for keys 16*kk + 8*r + 4*(l>>5) .. +3.
+  // holds column 32*cb + (l&31) for keys 16*kk + 8*r + 4*(l>>5) .. +3.  This wave's column
+  // blocks are cb = 8*half + cbl; the half offset is folded into the base.
   int vaddr[2][2];
   {
     const int G = lane >> 4, j = lane & 15;
@@ -379,146 +414,178 @@ void mla_verify_partial(PartialArgs p) {
     for (int e = 0; e < 2; ++e)
 #pragma unroll
       for (int r = 0; r < 2; ++r)
-        vaddr[e][r] = r * kKeyBlockBytes + kr * 128 + (((4 * e) ^ u ^ kr ^ r) << 4) + (j & 1) * 8;
+        vaddr[e][r] = half * 4 * kBlockBytes + r * kKeyBlockBytes + kr * 128 + (((4 * e) ^ u ^ kr ^ r) << 4) +
+                      (j & 1) * 8;
   }
 
-  f32x16 o[kColBlocks];
+  // O^T accumulators: columns [256*half, +256) for the wave's own 32 rows and the partner's 32 rows
+  f32x16 o_own[kHalfColBlocks], o_par[kHalfColBlocks];
 #pragma unroll
-  for (int cb = 0; cb < kColBlocks; ++cb) o[cb] = (f32x16){};
+  for (int c = 0; c < kHalfColBlocks; ++c) {
+    o_own[c] = (f32x16){};
+    o_par[c] = (f32x16){};
+  }
   // Softmax with a fixed per-row reference: m_ref is the row max of the split's
   // first tile with a visible key; p = 2^(x - m_ref) is exact as long as no
   // later score exceeds m_ref by more than kRefHeadroom.  A row that does is
   // recomputed exactly at the end (redo_rows_exact).
-  RowSoftmax st{-INFINITY, 0.f, 0.f, false, 0.f};
+  RowSoftmax st{-INFINITY, 0.f, 0.f, false};
 
-  const int32_t* slots_g = p.slot_idx + wi.ko;
-  for (int c0 = wi.t_begin; c0 < wi.t_end; c0 += kChunkKeys / kTileKeys) {
-    const int c1 = min(wi.t_end, c0 + kChunkKeys / kTileKeys);  // tiles [c0, c1) in this chunk
-    const int ntiles = c1 - c0;
-    // stage the chunk's slot indices (ragged tail: repeat the last key, masked out below)
-    __syncthreads();  // the previous chunk is fully consumed
-    for (int i = tid; i < ntiles * kTileKeys; i += kWaves * 64) {
-      const int key = min(c0 * kTileKeys + i, L - 1);
-      slot_lds[i] = slots_g[key];
-    }
-    __syncthreads();
-    auto slot_of = [&](int t) { return slot_lds[(t - c0) * kTileKeys + w * 8 + g_kr]; };
-    const int nfirst = min(ntiles, kAhead);
-    for (int t = 0; t < nfirst; ++t) issue_tile(t, slot_of(c0 + t));
-    int slot_next = ntiles > kAhead ? slot_of(c0 + kAhead) : 0;
+  bf16x8 kf[kQkSteps];
+  auto kread = [&](const lds_char* tb, int ks) {
+    kf[ks] = *(const __attribute__((address_space(3))) bf16x8*)(tb + kaddr[ks & 3] + (ks >> 2) * kBlockBytes);
+  };
 
-    // tile c0 must be complete before its Q.K
-    if (nfirst == 3) MLAV_WAIT_VMCNT(2 * kDmaPerTile);
-    else if (nfirst == 2) MLAV_WAIT_VMCNT(kDmaPerTile);
+  // tile 0 published, Q.K of tile 0; then tile 1 published for the first step
+  if (nfirst == 3) MLAV_WAIT_VMCNT(2 * kDmaPerTile);
+  else if (nfirst == 2) MLAV_WAIT_VMCNT(kDmaPerTile);
+  else MLAV_WAIT_VMCNT(0);
+  __syncthreads();
+  f32x16 sacc;
+#pragma unroll
+  for (int ks = 0; ks < kPrefetch; ++ks) kread(smem, ks);
+#pragma unroll
+  for (int ks = 0; ks < kQkSteps; ++ks) {
+    __builtin_amdgcn_sched_barrier(0);
+    if (ks + kPrefetch < kQkSteps) kread(smem, ks + kPrefetch);
+    __builtin_amdgcn_sched_barrier(0);
+    if (ks == 0) mfma_first_v(sacc, kf[ks], qf[ks]);
+    else mfma_acc_v(sacc, kf[ks], qf[ks]);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  if (ntiles > 1) {
+    if (nfirst == 3) MLAV_WAIT_VMCNT(kDmaPerTile);
     else MLAV_WAIT_VMCNT(0);
     __syncthreads();
+  }
 
-    bf16x8 kf[kQkSteps];
-    auto kread = [&](const lds_char* tb, int ks) {
-      kf[ks] = *(const __attribute__((address_space(3))) bf16x8*)(tb + kaddr[ks & 3] + (ks >> 2) * kBlockBytes);
-    };
-    f32x16 sacc;
-    {
-      const lds_char* tb = smem;
+  for (int i = 0; i < ntiles; ++i) {
+    const int t = wi.t_begin + i;
+    const lds_char* tb = smem + (i & (kRing - 1)) * kTileBytes;
+    const int key0 = t * kTileKeys + 4 * hi;
+    asm volatile(MLAV_MFMA_DRAIN : "+v"(sacc));
+    SoftmaxTile sm;
+    sm.s = sacc;
+    if (t * kTileKeys + kTileKeys > mask_from) mask_tile(sm.s, key0, limit);
+
+    // ---- phase A: Q.K of tile i+1 with the softmax of tile i between its MFMAs ----
+    if (i + 1 < ntiles) {
+      const lds_char* nb = smem + ((i + 1) & (kRing - 1)) * kTileBytes;
+      f32x16 snext;
 #pragma unroll
-      for (int ks = 0; ks < kPrefetch; ++ks) kread(tb, ks);
+      for (int ks = 0; ks < kPrefetch; ++ks) kread(nb, ks);
 #pragma unroll
       for (int ks = 0; ks < kQkSteps; ++ks) {
         __builtin_amdgcn_sched_barrier(0);
-        if (ks + kPrefetch < kQkSteps) kread(tb, ks + kPrefetch);
+        if (ks + kPrefetch < kQkSteps) kread(nb, ks + kPrefetch);
         __builtin_amdgcn_sched_barrier(0);
-        if (ks == 0) mfma_first_v(sacc, kf[ks], qf[ks]);
-        else mfma_acc_v(sacc, kf[ks], qf[ks]);
+        if (ks == 0) mfma_first_v(snext, kf[ks], qf[ks]);
+        else mfma_acc_v(snext, kf[ks], qf[ks]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (ks < kSoftmaxSlots) softmax_slot(ks, sm, st, p.scale_log2);
       }
       __builtin_amdgcn_sched_barrier(0);
+      sacc = snext;
+    } else {
+#pragma unroll
+      for (int slot = 0; slot < kSoftmaxSlots; ++slot) softmax_slot(slot, sm, st, p.scale_log2);
     }
+    // publish this wave's P (B-operand layout) for its partner
+    lds_char* xw = xchg + (i & 1) * (kWaves * 2048) + w * 2048 + lane * 16;
+    *(__attribute__((address_space(3))) i32x4*)(xw) = sm.operand(0);
+    *(__attribute__((address_space(3))) i32x4*)(xw + 1024) = sm.operand(1);
 
-    for (int i = 0; i < ntiles; ++i) {
-      const int t = c0 + i;
-      const lds_char* tb = smem + (i & (kRing - 1)) * kTileBytes;
-      const int key0 = t * kTileKeys + 4 * hi;
-      asm volatile(MLAV_MFMA_DRAIN : "+v"(sacc));
-      SoftmaxTile sm;
-      sm.s = sacc;
-      if (t * kTileKeys + kTileKeys > mask_from) mask_tile(sm.s, key0, limit);
-      if (i + 1 < ntiles) {
-        // tile i+1 complete (its loads are the oldest still counted), then publish it
-        if (i + 2 < ntiles) MLAV_WAIT_VMCNT(kDmaPerTile);
-        else MLAV_WAIT_VMCNT(0);
-        __syncthreads();
-        const bool refill = i + kAhead < ntiles;
-        const uint32_t dma_base = smem_base + ((i + kAhead) & (kRing - 1)) * kTileBytes + w_uniform * kKeyBlockBytes;
-        const char* dma_row = kv + (int64_t)slot_next * kRowBytes + g_byte;
-        // Q.K of tile i+1; between its MFMAs: the softmax of tile i and the
-        // loads that refill the ring with tile i+kAhead
-        const lds_char* nb = smem + ((i + 1) & (kRing - 1)) * kTileBytes;
-        f32x16 snext;
-#pragma unroll
-        for (int ks = 0; ks < kPrefetch; ++ks) kread(nb, ks);
-#pragma unroll
-        for (int ks = 0; ks < kQkSteps; ++ks) {
-          __builtin_amdgcn_sched_barrier(0);
-          if (ks + kPrefetch < kQkSteps) kread(nb, ks + kPrefetch);
-          __builtin_amdgcn_sched_barrier(0);
-          if (ks == 0) mfma_first_v(snext, kf[ks], qf[ks]);
-          else mfma_acc_v(snext, kf[ks], qf[ks]);
-          __builtin_amdgcn_sched_barrier(0);
-          if (ks < kSoftmaxSlots) softmax_slot(ks, sm, st, p.scale_log2);
-          if (ks >= 1 && ks <= kDmaPerTile && refill) dma16(dma_row + (ks - 1) * 128, dma_base + (ks - 1) * kBlockBytes);
-          if (ks == kDmaPerTile + 1 && i + kAhead + 1 < ntiles) slot_next = slot_of(t + kAhead + 1);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        sacc = snext;
-      } else {
-#pragma unroll
-        for (int slot = 0; slot < kSoftmaxSlots; ++slot) softmax_slot(slot, sm, st, p.scale_log2);
-      }
-      bf16x8 pf[2] = {__builtin_bit_cast(bf16x8, sm.pk[0]), __builtin_bit_cast(bf16x8, sm.pk[1])};
+    // tile i+2 complete and every wave's P written, then publish
+    MLAV_WAIT_VMCNT(0);
+    __syncthreads();
 
-      // O^T += V^T . P^T over tile i (fragment n: column block n%16, 16-key step n/16)
-      bf16x8 vf[kPvSteps];
-      auto vread = [&](int n) {
-        const int cb = n & (kColBlocks - 1), kk = n >> 4;
-        const lds_char* vb = tb + (cb >> 1) * kBlockBytes + kk * 2 * kKeyBlockBytes;
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4*)(vb + vaddr[cb & 1][0]));
-        const i16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4*)(vb + vaddr[cb & 1][1]));
-        vf[n] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
-      };
+    // ---- phase B: P.V of tile i for the pair's 64 rows x this wave's 256 columns;
+    //      the loads that refill the ring with tile i+3 go between its MFMAs ----
+    const bf16x8 pown[2] = {__builtin_bit_cast(bf16x8, sm.operand(0)), __builtin_bit_cast(bf16x8, sm.operand(1))};
+    bf16x8 ppar[2];
+    {
+      const lds_char* xp = xchg + (i & 1) * (kWaves * 2048) + partner * 2048 + lane * 16;
+      ppar[0] = *(const __attribute__((address_space(3))) bf16x8*)(xp);
+      ppar[1] = *(const __attribute__((address_space(3))) bf16x8*)(xp + 1024);
+    }
+    // V^T fragment n: local column block n%8, 16-key step n/8
+    bf16x8 vf[kPvFrags];
+    auto vread = [&](int n) {
+      const int cbl = n & (kHalfColBlocks - 1), kk = n >> 3;
+      const lds_char* vb = tb + (cbl >> 1) * kBlockBytes + kk * 2 * kKeyBlockBytes;
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4*)(vb + vaddr[cbl & 1][0]));
+      const i16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4*)(vb + vaddr[cbl & 1][1]));
+      vf[n] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
 #pragma unroll
-      for (int n = 0; n < kPrefetch; ++n) vread(n);
-#pragma unroll
-      for (int n = 0; n < kPvSteps; ++n) {
-        __builtin_amdgcn_sched_barrier(0);
-        if (n + kPrefetch < kPvSteps) vread(n + kPrefetch);
-        __builtin_amdgcn_sched_barrier(0);
-        mfma_acc_a(o[n & (kColBlocks - 1)], vf[n], pf[n >> 4]);
+    for (int n = 0; n < kVPrefetch; ++n) vread(n);
+    __builtin_amdgcn_sched_barrier(0);
+    // refill the ring with tile i+3 (its buffer held tile i-1, which every wave has finished)
+    if (i + kAhead < ntiles) {
+      if (((i + kAhead) & 7) == 0) {  // the next 8 tiles' slot indices
+        sv_cur = sv_next;
+        sv_next = load_slots(i + kAhead + 8);
       }
+      issue_tile((i + kAhead) & (kRing - 1), slot_for(sv_cur, i + kAhead));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int n = 0; n < kPvFrags; ++n) {
       __builtin_amdgcn_sched_barrier(0);
+      if (n + kVPrefetch < kPvFrags) vread(n + kVPrefetch);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_acc_a(o_own[n & (kHalfColBlocks - 1)], vf[n], pown[n >> 3]);
+      mfma_acc_a(o_par[n & (kHalfColBlocks - 1)], vf[n], ppar[n >> 3]);
     }
+    __builtin_amdgcn_sched_barrier(0);
   }
-  asm volatile(MLAV_MFMA_DRAIN : "+a"(o[kColBlocks - 1]));
+  asm volatile(MLAV_MFMA_DRAIN : "+a"(o_own[kHalfColBlocks - 1]), "+a"(o_par[kHalfColBlocks - 1]));
 
   // ---- partial write: o_s = O / l, lse_s = ln2 * (m_ref + log2 l) -------------------------------
-  if (!row_valid) return;
+  // The row sums live with the row's owner wave; swap them through LDS.
   const float lt = pair_sum(st.l_run);
   const float le = pair_sum(st.l_exact);
-  const float inv = lt > 0.f ? 1.0f / lt : 0.f;
-  const int64_t prow = ((int64_t)wi.bs * p.rows_pad + myrow);
-  float* dst = p.o_part + prow * kDv + 4 * hi;
+  __syncthreads();  // every wave is done reading the P exchange buffers
+  float* lsum = (float*)(smem_raw + kRing * kTileBytes);
+  if (hi == 0) lsum[w * 32 + lrow] = lt;
+  __syncthreads();
+  const float lt_par = lsum[partner * 32 + lrow];
+  const float inv_own = lt > 0.f ? 1.0f / lt : 0.f;
+  const float inv_par = lt_par > 0.f ? 1.0f / lt_par : 0.f;
+  const int col0 = half * (kDv / 2) + 4 * hi;
+  if (row_valid) {
+    float* dst = p.o_part + ((int64_t)wi.bs * p.rows_pad + myrow) * kDv + col0;
 #pragma unroll
-  for (int cb = 0; cb < kColBlocks; ++cb)
+    for (int c = 0; c < kHalfColBlocks; ++c)
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      f32x4 v = {o[cb][4 * q4 + 0] * inv, o[cb][4 * q4 + 1] * inv, o[cb][4 * q4 + 2] * inv, o[cb][4 * q4 + 3] * inv};
-      *(f32x4*)(dst + cb * 32 + 8 * q4) = v;
-    }
-  if (hi == 0) p.lse_part[prow] = le > 0.f ? (st.m_ref + __builtin_amdgcn_logf(le)) * kLn2 : -INFINITY;
+      for (int q4 = 0; q4 < 4; ++q4) {
+        f32x4 v = {o_own[c][4 * q4] * inv_own, o_own[c][4 * q4 + 1] * inv_own, o_own[c][4 * q4 + 2] * inv_own,
+                   o_own[c][4 * q4 + 3] * inv_own};
+        *(f32x4*)(dst + c * 32 + 8 * q4) = v;
+      }
+    if (hi == 0)
+      p.lse_part[(int64_t)wi.bs * p.rows_pad + myrow] =
+          le > 0.f ? (st.m_ref + __builtin_amdgcn_logf(le)) * kLn2 : -INFINITY;
+  }
+  if (parrow < R) {
+    float* dst = p.o_part + ((int64_t)wi.bs * p.rows_pad + parrow) * kDv + col0;
+#pragma unroll
+    for (int c = 0; c < kHalfColBlocks; ++c)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        f32x4 v = {o_par[c][4 * q4] * inv_par, o_par[c][4 * q4 + 1] * inv_par, o_par[c][4 * q4 + 2] * inv_par,
+                   o_par[c][4 * q4 + 3] * inv_par};
+        *(f32x4*)(dst + c * 32 + 8 * q4) = v;
+      }
+  }
 
-  // Rows whose scores outgrew the fixed reference are redone exactly by the wave.
-  const uint64_t redo = __ballot(st.overflow && hi == 0);
-  if (redo != 0) redo_rows_exact(p, wi, wi.g * kRowsPerGroup + w * kRowsPerWave, (uint32_t)redo);
+  // Rows whose scores outgrew the fixed reference are redone exactly by their owner
+  // wave, once both halves of the row have been written.
+  const uint64_t redo = __ballot(st.overflow && hi == 0 && row_valid);
+  __syncthreads();  // (global writes of both halves are ordered by the barrier's release/acquire)
+  if (redo != 0) redo_rows_exact(p, wi, row0 + w * kRowsPerWave, (uint32_t)redo);
 }
 
 __global__ __launch_bounds__(256) void mla_verify_merge_kernel(MergeArgs p) {
