@@ -39,6 +39,28 @@ def algorithmic_counts(x):
     return flops, kv_bytes, alg_bytes
 
 
+def measured_traffic(workload: str):
+    """HBM bytes per kernel-1 launch from the committed rocprofv3 counter summary, or None.
+
+    The summary records the sha256 of the kernel source it was taken on; once the
+    source differs, the counters no longer describe the kernel and None is returned.
+    """
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"mla_verify_partial_{workload}_traffic.md")
+    src = os.path.join(ROOT, "speculative_decode_mla_amd", "csrc", "mla_verify_kernels.hip")
+    if not (os.path.exists(path) and os.path.exists(src)):
+        return None
+    fields = {}
+    for line in open(path):
+        key, sep, val = line.partition(":")
+        if sep and key.strip() in ("kernel_source_sha256", "traffic_bytes_per_launch"):
+            fields[key.strip()] = val.strip()
+    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if fields.get("kernel_source_sha256") != digest or "traffic_bytes_per_launch" not in fields:
+        return None
+    return int(fields["traffic_bytes_per_launch"])
+
+
 def cpu_baseline(x, budget_s: float):
     """Time the oracle on the first k draft tokens of request 0 (their exact key ranges); extrapolate."""
     import oracle
@@ -225,7 +247,8 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "mla_verify_partial",
                      "achieved": round(k1_tflops, 1) if k1_tflops else None, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(k1_tflops / PEAK_BF16_TFLOPS, 4) if k1_tflops else None,
-                     "traffic": None, "flops_per_launch": flops},
+                     "traffic": measured_traffic(w.name), "traffic_unit": "bytes/launch",
+                     "flops_per_launch": flops},
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(x, args.cpu_budget)

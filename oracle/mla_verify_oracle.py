@@ -25,7 +25,7 @@ What it computes (the pages' subject, restated):
     unsplit definition below is the result; `verify_attention_split` follows
     the partial + reduce steps for the split/unsplit pin.
 
-Readings where the pages are silent (each is listed in the design doc):
+Readings where the pages are silent:
   * seq_lens[b] counts the request's draft tokens; their rows are the last
     q_lens[b] entries of the request's slot list.
   * Causal within the draft block, inclusive: draft t (0-based) sees keys
