@@ -23,16 +23,27 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (set HIPCC or install ROCm)")
 
 
+COMMON_FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17",
+    # keep packed fp32 VALU ops out of the generated code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"),
+]
+
+
+def device_asm(source: str, out_path: str) -> str:
+    """gfx950 assembly of one source file with the library's flags (for inspection and checks)."""
+    cmd = [hipcc(), *COMMON_FLAGS, "--cuda-device-only", "-S", source, "-o", out_path]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc -S failed ({r.returncode}):\n{r.stderr}")
+    return out_path
+
+
 def build(verbose: bool = False) -> str:
     """Compile the library; returns its path.  Always recompiles."""
     tmp = LIB + ".tmp"
-    cmd = [
-        hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-        # keep packed fp32 VALU ops out of the generated code
-        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-        "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"),
-        *SOURCES, "-o", tmp,
-    ]
+    cmd = [hipcc(), *COMMON_FLAGS, "-fPIC", "-shared", *SOURCES, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -10,12 +10,12 @@
 // CDNA4 rather than for the sm_120 part the page targets.
 //
 // Kernel 1, one workgroup = 4 waves (one per SIMD), 32 (token, head) rows per wave:
-//   * Slot staging: the split's slot indices (up to 4096 at a time) are copied
-//     to LDS once, so the gather never waits on a global index load.
+//   * Slot indices: each lane holds one slot of each of the next 8 tiles; a
+//     shuffle hands every gathering lane its key's slot.
 //   * Gather: 32 keys per tile.  Each key's 1152-B latent row (9 whole 128-B
 //     lines) goes straight from HBM into LDS with 16-B direct-to-LDS loads,
-//     8 lanes per 128-B line.  A ring of 4 tile buffers; the load of tile i+3
-//     is issued while tile i is being consumed.
+//     8 lanes per 128-B line, 8 keys per wave.  A ring of 4 tile buffers; the
+//     load of tile i+3 is issued while tile i is being consumed.
 //   * LDS tile layout: key k (0..31), 16-B chunk c (0..71) of its row lives at
 //       ((k/8)*9 + c/8)*1024 + (k%8)*128 + ((c%8) ^ f(k))*16,  f(k) = (k%8) ^ ((k/8)%2)
 //     so one load instruction fills one 1 KiB block (8 keys x 128 B), and the
@@ -26,14 +26,17 @@
 //     layout each lane then holds one row and 16 keys; lanes l and l^32 share a
 //     row.
 //   * Softmax in base 2 with the scale folded in, against a per-row reference
-//     max fixed at the split's first tile with a visible key; the exponentials
-//     of tile i are computed while the MFMA unit runs Q.K of tile i+1.  Causal
-//     mask on the draft block (keys >= L - Q + 1).
+//     max fixed at the split's first tile (no rescale of the accumulators; a
+//     row whose sum outgrows it is redone exactly).  The exponentials of tile i
+//     are computed between the Q.K MFMAs of tile i+1, its row sums between its
+//     own P.V MFMAs.  Causal mask on the draft block (keys >= L - Q + 1).
 //   * P.V as O^T = V^T . P^T: the probabilities stay in registers as the B
 //     operand (the S^T C layout is a valid B layout after a fixed permutation
 //     of the key order, which the V^T operand repeats), and V^T fragments come
 //     from LDS with ds_read_b64_tr_b16, which transposes 4x16 blocks of bf16
-//     across each 16-lane group.
+//     across each 16-lane group.  Waves 2k and 2k+1 form a pair: each computes
+//     256 of the 512 output columns for the pair's 64 rows, taking its
+//     partner's P through LDS, so each wave reads only half of V.
 #include "mla_verify_internal.h"
 
 namespace mlav {
@@ -101,19 +104,51 @@ __device__ __forceinline__ float pair_sum(float v) {
 
 // MFMA 32x32x16 bf16 issued through inline asm so that the accumulator stays in
 // the register class chosen here: the 256-register output accumulator in
-// AGPRs, the per-tile scores in VGPRs.  The compiler does not look inside
-// these statements, so the wait states it would otherwise insert are given
-// explicitly: "s_nop 2" ahead of each MFMA covers a VALU write of an operand
-// register just before it, and MLAV_MFMA_DRAIN covers an MFMA result read by
-// VALU code.
+// AGPRs, the per-tile scores in VGPRs.  The statements are volatile so that
+// they keep their order relative to the softmax statements below, which sit
+// between them on purpose.  The compiler does not look inside these statements,
+// so it inserts no wait states for them.  Two hazards matter: a VALU write of
+// an operand register just before an MFMA, and a VALU read of an MFMA result.
+// The second is covered by MLAV_MFMA_DRAIN wherever scores or accumulators are
+// read.  The first does not arise in the schedule below (operands come from LDS
+// reads, which are waited on with lgkmcnt, from the resident q fragments, or
+// from bf16 packs made many instructions earlier); tests/test_kernel_hazards.py
+// checks the generated code for both.  Only the first MFMA of a tile keeps a
+// guard, since it follows the softmax code directly.
 __device__ __forceinline__ void mfma_acc_a(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-  asm("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 __device__ __forceinline__ void mfma_acc_v(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-  asm("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
 }
 __device__ __forceinline__ void mfma_first_v(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-  asm("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(acc) : "v"(a), "v"(b));
+  asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(acc) : "v"(a), "v"(b));
+}
+
+// Single VALU ops as volatile statements, so that each stays in the MFMA gap it
+// is written in (the compiler would otherwise gather them into one block).
+// None of them has a wait-state requirement towards its neighbours except the
+// exp2: its result is read no earlier than after the next MFMA.
+__device__ __forceinline__ float vfma(float x, float s, float c) {
+  float r;
+  asm volatile("v_fma_f32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(s), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float vexp2(float x) {
+  float r;
+  asm volatile("v_exp_f32 %0, %1" : "=v"(r) : "v"(x));
+  return r;
+}
+__device__ __forceinline__ int vpack_bf16(float lo, float hi) {  // round to nearest even
+  int r;
+  asm volatile("v_cvt_pk_bf16_f32 %0, %1, %2" : "=v"(r) : "v"(lo), "v"(hi));
+  return r;
+}
+__device__ __forceinline__ void vadd_to(float& acc, float x) {
+  asm volatile("v_add_f32 %0, %0, %1" : "+v"(acc) : "v"(x));
+}
+__device__ __forceinline__ void vsum_pair_to(float& acc, int pair) {  // acc += lo + hi of a bf16 pair
+  asm volatile("v_dot2c_f32_bf16 %0, 0x3f803f80, %1" : "+v"(acc) : "v"(pair));
 }
 // 24 wait states: an MFMA result may now be read by VALU / accvgpr moves.
 #define MLAV_MFMA_DRAIN "s_nop 7\n\ts_nop 7\n\ts_nop 7"
@@ -142,6 +177,20 @@ __device__ __forceinline__ void dma16(const void* gsrc, uint32_t m0_value) {
 
 // One wave's share of a tile: key block w (8 keys x 1152 B) as nine 1 KiB loads;
 // load cg moves 16-B chunks [8cg, 8cg+8) of the eight rows (see the layout above).
+// dma_chunk_group issues load cg alone (cg a compile-time constant after unrolling).
+__device__ __forceinline__ void dma_chunk_group(const char* row, uint32_t lds_block, int cg) {
+  switch (cg) {
+    case 0: dma16<0 * 128>(row, lds_block + 0 * (kBlockBytes - 128)); break;
+    case 1: dma16<1 * 128>(row, lds_block + 1 * (kBlockBytes - 128)); break;
+    case 2: dma16<2 * 128>(row, lds_block + 2 * (kBlockBytes - 128)); break;
+    case 3: dma16<3 * 128>(row, lds_block + 3 * (kBlockBytes - 128)); break;
+    case 4: dma16<4 * 128>(row, lds_block + 4 * (kBlockBytes - 128)); break;
+    case 5: dma16<5 * 128>(row, lds_block + 5 * (kBlockBytes - 128)); break;
+    case 6: dma16<6 * 128>(row, lds_block + 6 * (kBlockBytes - 128)); break;
+    case 7: dma16<7 * 128>(row, lds_block + 7 * (kBlockBytes - 128)); break;
+    default: dma16<8 * 128>(row, lds_block + 8 * (kBlockBytes - 128)); break;
+  }
+}
 __device__ __forceinline__ void dma_key_block(const char* row, uint32_t lds_block) {
   dma16<0 * 128>(row, lds_block + 0 * (kBlockBytes - 128));
   dma16<1 * 128>(row, lds_block + 1 * (kBlockBytes - 128));
@@ -201,10 +250,11 @@ __device__ __forceinline__ bool decode_work(const PartialArgs& p, int wg, WorkIt
   return true;
 }
 
-// Exact recomputation of rows whose scores rose more than kRefHeadroom above
-// the row's reference max: one row at a time across the whole wave, with a
-// running max and a rescale at every key, in fp32.  Overwrites the row's partial.
-// Only reached for such rows, so its speed does not matter.
+// Exact recomputation of rows whose fixed-reference row sum reached
+// kRowSumLimit (scores far above the max of the split's first tile): one row at
+// a time across the whole wave, with a running max and a rescale at every key,
+// in fp32.  Overwrites the row's partial.  Only reached for such rows, so its
+// speed does not matter.
 __device__ __forceinline__ void redo_rows_exact(const PartialArgs& p, const WorkItem& wi, int row_base, uint32_t rows) {
   const int lane = threadIdx.x & 63;
   const int key_begin = wi.t_begin * kTileKeys;
@@ -246,81 +296,59 @@ __device__ __forceinline__ void redo_rows_exact(const PartialArgs& p, const Work
 }
 
 // Per-row softmax state of one lane (row lrow; the lane pair l, l^32 agrees on
-// every field but the two partial sums).
+// m_ref and holds half of each row sum).
 struct RowSoftmax {
-  float m_ref;    // reference max (log2 units), -inf until a visible key is seen
+  float m_ref;    // reference max (log2 units): the row max of the split's first tile; -inf if none is visible
   float l_run;    // this lane's share of the row sum of bf16-rounded P (normalises O)
   float l_exact;  // ... and of P before rounding (gives the LSE)
-  bool overflow;  // a score exceeded m_ref + kRefHeadroom: redo the row exactly
 };
 
-// Headroom (log2 units) above a row's reference max before exp2 could overflow
-// the fp32 sums: p = 2^(x - m_ref) <= 2^64, times <= 2^31 keys, stays finite.
-constexpr float kRefHeadroom = 64.0f;
+// p = 2^(x - m_ref) is used as is, with no rescale, as long as the row sums stay
+// below 2^64: then every p is below 2^64 and, over at most 2^31 keys, neither
+// the sums nor the output accumulators can overflow fp32.  A row whose sum
+// reaches it (including +inf from an overflowing exp2) is redone exactly.
+constexpr float kRowSumLimit = 18446744073709551616.0f;  // 2^64
 
-// Softmax of one tile, cut into kSoftmaxSlots slices that are placed between the
-// Q.K MFMAs of the next tile (one slice per MFMA).  A VALU op costs the wave 4
-// cycles (an exp 8) and only about 20 cycles of VALU fit under one 32-cycle MFMA,
-// so each slice is kept to a few independent ops:
-//   0..3  row max of the raw scores (max3 tree, lane pair), reference update
-//   4+j   x_j = s_j * scale - m_ref        (one FMA; the scale is folded in here)
-//   5+j   p_j = 2^x_j
-//   6+j   exact row sum; for odd j, bf16 pack of (p_{j-1}, p_j)
-//   7+j   for odd j, rounded row sum of the pair (v_dot2_f32_bf16 with (1, 1))
+// Row max of a tile's raw scores: 16 values per lane, then the lane pair.
+__device__ __forceinline__ float tile_row_max(const f32x16& s) {
+  float m0 = fmaxf(fmaxf(s[0], s[1]), s[2]);
+  float m1 = fmaxf(fmaxf(s[3], s[4]), s[5]);
+  float m2 = fmaxf(fmaxf(s[6], s[7]), s[8]);
+  m0 = fmaxf(fmaxf(m0, s[9]), s[10]);
+  m1 = fmaxf(fmaxf(m1, s[11]), s[12]);
+  m2 = fmaxf(fmaxf(m2, s[13]), s[14]);
+  m0 = fmaxf(fmaxf(m0, m1), fmaxf(m2, s[15]));
+  return pair_max(m0);
+}
+
+// Softmax of one tile, cut into slices placed between MFMAs.  With one wave per
+// SIMD, an MFMA hides a few independent VALU ops of the same wave but not a
+// long block of them, so the work is spread thin.  The slices that make P sit
+// between the Q.K MFMAs of the next tile (softmax_slot, slot k):
+//   x_k = s_k * scale - m_ref         (one FMA; the scale is folded in here)
+//   p_{k-1} = 2^(x_{k-1})
+//   for k-2 odd: bf16 pack of (p_{k-3}, p_{k-2})   (both made in earlier slots)
+// and the row sums sit between the P.V MFMAs of the same tile (sum_slot):
+//   exact sum += p_n; for odd n, rounded sum += the packed pair.
 // The causal mask is applied to the raw scores beforehand, on the tiles that
 // reach the draft block only.
-constexpr int kSoftmaxSlots = 23;
+constexpr int kSoftmaxSlots = 18;
 struct SoftmaxTile {
   f32x16 s;       // raw scores -> 2^(s*scale - m_ref)
-  float m[3];     // max tree
-  float nmref;    // -m_ref (0 while m_ref is -inf)
   int pw[8];      // bf16 pairs; pw[0..3], pw[4..7] are the MFMA B operands of the two 16-key steps
                   // (kept as separate scalars: element inserts into a vector here were miscompiled)
   __device__ i32x4 operand(int kk) const { return (i32x4){pw[4 * kk], pw[4 * kk + 1], pw[4 * kk + 2], pw[4 * kk + 3]}; }
 };
 
-__device__ __forceinline__ void softmax_slot(int slot, SoftmaxTile& t, RowSoftmax& st, float scale_log2) {
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  if (slot == 0) {
-    t.m[0] = fmaxf(fmaxf(t.s[0], t.s[1]), t.s[2]);
-    t.m[1] = fmaxf(fmaxf(t.s[3], t.s[4]), t.s[5]);
-    t.m[2] = fmaxf(fmaxf(t.s[6], t.s[7]), t.s[8]);
-    t.m[0] = fmaxf(fmaxf(t.m[0], t.s[9]), t.s[10]);
-    t.m[1] = fmaxf(fmaxf(t.m[1], t.s[11]), t.s[12]);
-    return;
-  }
-  if (slot == 1) {
-    t.m[2] = fmaxf(fmaxf(t.m[2], t.s[13]), t.s[14]);
-    t.m[0] = fmaxf(fmaxf(t.m[0], t.m[1]), t.s[15]);
-    t.m[0] = fmaxf(t.m[0], t.m[2]);
-    return;
-  }
-  if (slot == 2) {
-    t.m[0] = pair_max(t.m[0]) * scale_log2;  // scale > 0 commutes with max
-    return;
-  }
-  if (slot == 3) {
-    const float mx = t.m[0];
-    st.m_ref = (st.m_ref == -INFINITY) ? mx : st.m_ref;
-    st.overflow |= mx > st.m_ref + kRefHeadroom;
-    t.nmref = (st.m_ref == -INFINITY) ? 0.f : -st.m_ref;
-    return;
-  }
-  const int a = slot - 4, b = slot - 5, c = slot - 6, d = slot - 7;
-  if (a >= 0 && a < 16) t.s[a] = __builtin_fmaf(t.s[a], scale_log2, t.nmref);
-  if (b >= 0 && b < 16) t.s[b] = __builtin_amdgcn_exp2f(t.s[b]);
-  if (c >= 0 && c < 16) {
-    st.l_exact += t.s[c];
-    if (c & 1) {
-      const bf16x2 pr = {(__bf16)t.s[c - 1], (__bf16)t.s[c]};
-      t.pw[c >> 1] = __builtin_bit_cast(int, pr);
-    }
-  }
-  if (d >= 0 && d < 16 && (d & 1)) {
-    const bf16x2 pr = __builtin_bit_cast(bf16x2, t.pw[d >> 1]);
-    const bf16x2 one = __builtin_bit_cast(bf16x2, 0x3f803f80);
-    st.l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, one, st.l_run, false);
-  }
+__device__ __forceinline__ void softmax_slot(int k, SoftmaxTile& t, float nmref, float scale_log2) {
+  if (k < 16) t.s[k] = vfma(t.s[k], scale_log2, nmref);
+  if (k >= 1 && k <= 16) t.s[k - 1] = vexp2(t.s[k - 1]);
+  if (k >= 3 && k <= 17 && ((k - 2) & 1)) t.pw[(k - 2) >> 1] = vpack_bf16(t.s[k - 3], t.s[k - 2]);
+}
+
+__device__ __forceinline__ void sum_slot(int n, const SoftmaxTile& t, RowSoftmax& st) {
+  vadd_to(st.l_exact, t.s[n]);
+  if (n & 1) vsum_pair_to(st.l_run, t.pw[n >> 1]);
 }
 
 // Causal mask on the raw scores of a tile that reaches the draft block:
@@ -364,23 +392,29 @@ void mla_verify_partial(PartialArgs p) {
   const char* kv = (const char*)p.kv;
   const uint32_t smem_base = (uint32_t)(uintptr_t)smem;
   const int w_uniform = __builtin_amdgcn_readfirstlane(w);
-  // Slot indices, 8 tiles per register: lane j holds the slot of key 8w + (j&7) of tile (base + j/8).
+  // Slot index of the row this lane gathers in tile i of the split: key 8w + g_kr of the tile.
+  // Past the request's last key (ragged tail, or refills beyond the split) it is the last
+  // key's row: a valid address whose scores are masked, or a buffer that is never read.
   const int32_t* slots_g = p.slot_idx + wi.ko;
-  auto load_slots = [&](int first_tile) {
-    int key = (wi.t_begin + first_tile + (lane >> 3)) * kTileKeys + w * 8 + (lane & 7);
-    key = key < L ? key : L - 1;  // ragged tail / past the split: any valid row (masked out below)
+  auto gather_slot = [&](int i) {
+    int key = (wi.t_begin + i) * kTileKeys + w * 8 + g_kr;
+    key = key < L ? key : L - 1;
     return slots_g[key];
   };
-  auto slot_for = [&](int sv, int i) { return __shfl(sv, 8 * (i & 7) + g_kr); };
   auto issue_tile = [&](int buf, int slot) {
     const uint32_t base = smem_base + buf * kTileBytes + w_uniform * kKeyBlockBytes;
     dma_key_block(kv + (int64_t)slot * kRowBytes + g_byte, base);
   };
 
-  int sv_cur = load_slots(0);
-  int sv_next = load_slots(8);
   const int nfirst = min(ntiles, kAhead);
-  for (int i = 0; i < nfirst; ++i) issue_tile(i, slot_for(sv_cur, i));
+  {
+    int sl[kAhead];
+#pragma unroll
+    for (int i = 0; i < kAhead; ++i) sl[i] = gather_slot(i);
+#pragma unroll
+    for (int i = 0; i < kAhead; ++i)
+      if (i < nfirst) issue_tile(i, sl[i]);
+  }
 
   // ---- the wave's 32 query rows, resident for the whole split ----------------------------------
   // lane holds row lrow, dims 16*ks + 8*hi .. +7 (MFMA B-operand layout)
@@ -426,10 +460,10 @@ void mla_verify_partial(PartialArgs p) {
     o_par[c] = (f32x16){};
   }
   // Softmax with a fixed per-row reference: m_ref is the row max of the split's
-  // first tile with a visible key; p = 2^(x - m_ref) is exact as long as no
-  // later score exceeds m_ref by more than kRefHeadroom.  A row that does is
+  // first tile (set after its Q.K below); p = 2^(x - m_ref) needs no rescale
+  // while the row sum stays below kRowSumLimit.  A row that reaches it is
   // recomputed exactly at the end (redo_rows_exact).
-  RowSoftmax st{-INFINITY, 0.f, 0.f, false};
+  RowSoftmax st{-INFINITY, 0.f, 0.f};
 
   bf16x8 kf[kQkSteps];
   auto kread = [&](const lds_char* tb, int ks) {
@@ -453,6 +487,17 @@ void mla_verify_partial(PartialArgs p) {
     else mfma_acc_v(sacc, kf[ks], qf[ks]);
   }
   __builtin_amdgcn_sched_barrier(0);
+  // The reference: the first tile's row max (masked).  If the row sees no key of
+  // that tile it sees none of the split (later tiles hold later keys): m_ref
+  // stays -inf, every p is 2^-inf = 0 and the partial is empty.
+  float nmref;
+  {
+    asm volatile(MLAV_MFMA_DRAIN : "+v"(sacc));
+    f32x16 s0 = sacc;
+    if (wi.t_begin * kTileKeys + kTileKeys > mask_from) mask_tile(s0, wi.t_begin * kTileKeys + 4 * hi, limit);
+    st.m_ref = tile_row_max(s0) * p.scale_log2;  // the scale is positive, so it commutes with the max
+    nmref = (st.m_ref == -INFINITY) ? 0.f : -st.m_ref;
+  }
   if (ntiles > 1) {
     if (nfirst == 3) MLAV_WAIT_VMCNT(kDmaPerTile);
     else MLAV_WAIT_VMCNT(0);
@@ -463,6 +508,10 @@ void mla_verify_partial(PartialArgs p) {
     const int t = wi.t_begin + i;
     const lds_char* tb = smem + (i & (kRing - 1)) * kTileBytes;
     const int key0 = t * kTileKeys + 4 * hi;
+    // Slot of the row this lane gathers for tile i+3, loaded now and awaited with the tile
+    // loads before the barrier below.  Past the end of the split it is still a valid row,
+    // which lands in the free ring buffer and is never read, so the refill needs no branch.
+    const int g_slot = gather_slot(i + kAhead);
     asm volatile(MLAV_MFMA_DRAIN : "+v"(sacc));
     SoftmaxTile sm;
     sm.s = sacc;
@@ -482,13 +531,13 @@ void mla_verify_partial(PartialArgs p) {
         if (ks == 0) mfma_first_v(snext, kf[ks], qf[ks]);
         else mfma_acc_v(snext, kf[ks], qf[ks]);
         __builtin_amdgcn_sched_barrier(0);
-        if (ks < kSoftmaxSlots) softmax_slot(ks, sm, st, p.scale_log2);
+        if (ks < kSoftmaxSlots) softmax_slot(ks, sm, nmref, p.scale_log2);
       }
       __builtin_amdgcn_sched_barrier(0);
       sacc = snext;
     } else {
 #pragma unroll
-      for (int slot = 0; slot < kSoftmaxSlots; ++slot) softmax_slot(slot, sm, st, p.scale_log2);
+      for (int slot = 0; slot < kSoftmaxSlots; ++slot) softmax_slot(slot, sm, nmref, p.scale_log2);
     }
     // publish this wave's P (B-operand layout) for its partner
     lds_char* xw = xchg + (i & 1) * (kWaves * 2048) + w * 2048 + lane * 16;
@@ -500,7 +549,8 @@ void mla_verify_partial(PartialArgs p) {
     __syncthreads();
 
     // ---- phase B: P.V of tile i for the pair's 64 rows x this wave's 256 columns;
-    //      the loads that refill the ring with tile i+3 go between its MFMAs ----
+    //      the nine loads that refill the ring with tile i+3 (into the buffer of tile
+    //      i-1, which every wave has finished) go between its MFMAs ----
     const bf16x8 pown[2] = {__builtin_bit_cast(bf16x8, sm.operand(0)), __builtin_bit_cast(bf16x8, sm.operand(1))};
     bf16x8 ppar[2];
     {
@@ -519,28 +569,25 @@ void mla_verify_partial(PartialArgs p) {
           (__attribute__((address_space(3))) i16x4*)(vb + vaddr[cbl & 1][1]));
       vf[n] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
     };
+    const char* g_row = kv + (int64_t)g_slot * kRowBytes + g_byte;
+    const uint32_t g_lds = smem_base + ((i + kAhead) & (kRing - 1)) * kTileBytes + w_uniform * kKeyBlockBytes;
 #pragma unroll
     for (int n = 0; n < kVPrefetch; ++n) vread(n);
-    __builtin_amdgcn_sched_barrier(0);
-    // refill the ring with tile i+3 (its buffer held tile i-1, which every wave has finished)
-    if (i + kAhead < ntiles) {
-      if (((i + kAhead) & 7) == 0) {  // the next 8 tiles' slot indices
-        sv_cur = sv_next;
-        sv_next = load_slots(i + kAhead + 8);
-      }
-      issue_tile((i + kAhead) & (kRing - 1), slot_for(sv_cur, i + kAhead));
-    }
-    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int n = 0; n < kPvFrags; ++n) {
       __builtin_amdgcn_sched_barrier(0);
       if (n + kVPrefetch < kPvFrags) vread(n + kVPrefetch);
       __builtin_amdgcn_sched_barrier(0);
       mfma_acc_a(o_own[n & (kHalfColBlocks - 1)], vf[n], pown[n >> 3]);
+      __builtin_amdgcn_sched_barrier(0);
+      sum_slot(n, sm, st);
+      if (n < kDmaPerTile) dma_chunk_group(g_row, g_lds, n);
+      __builtin_amdgcn_sched_barrier(0);
       mfma_acc_a(o_par[n & (kHalfColBlocks - 1)], vf[n], ppar[n >> 3]);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
+  MLAV_WAIT_VMCNT(0);  // the refills of the last steps (into free buffers) land before the workgroup ends
   asm volatile(MLAV_MFMA_DRAIN : "+a"(o_own[kHalfColBlocks - 1]), "+a"(o_par[kHalfColBlocks - 1]));
 
   // ---- partial write: o_s = O / l, lse_s = ln2 * (m_ref + log2 l) -------------------------------
@@ -583,7 +630,8 @@ void mla_verify_partial(PartialArgs p) {
 
   // Rows whose scores outgrew the fixed reference are redone exactly by their owner
   // wave, once both halves of the row have been written.
-  const uint64_t redo = __ballot(st.overflow && hi == 0 && row_valid);
+  const bool overflow = !(le < kRowSumLimit);  // some p reached 2^64, or an exp2 overflowed to +inf
+  const uint64_t redo = __ballot(overflow && hi == 0 && row_valid);
   __syncthreads();  // (global writes of both halves are ordered by the barrier's release/acquire)
   if (redo != 0) redo_rows_exact(p, wi, row0 + w * kRowsPerWave, (uint32_t)redo);
 }

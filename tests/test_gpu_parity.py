@@ -130,6 +130,17 @@ def test_overflow_fallback_rows(api):
     _check(api, x, 1, "overflow")
 
 
+def test_overflow_to_inf_fallback_rows(api):
+    """A key so far above the first tile's max that 2^(x - m_ref) overflows fp32:
+    without the exact fallback the row would come out inf/NaN."""
+    x = I.make_custom(np.random.default_rng(39), [3000], [4], 8, 6000)
+    q0 = oracle.bf16_bits_to_f64(x.q[2, 5])
+    # key 2900 aligned with (token 2, head 5): score ~ 2.6*|q|^2/sqrt(192) ~ 108 nats ~ 156 log2 units
+    x.kv_rows[2900] = I.f32_to_bf16_bits((2.6 * q0).astype(np.float32))
+    _check(api, x, 3, "overflow-inf")
+    _check(api, x, 1, "overflow-inf")
+
+
 def test_merge_kernel_alone(api):
     x = I.make_custom(np.random.default_rng(36), [400, 37], [5, 3], 6, 1000)
     S = 6

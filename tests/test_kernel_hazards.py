@@ -1,0 +1,53 @@
+"""The MFMAs are issued through inline asm, so the compiler inserts no wait
+states for them; check the generated gfx950 code for the MFMA hazards instead.
+CPU-only: it compiles the kernels to assembly, it runs nothing."""
+import os
+import shutil
+
+import pytest
+
+from speculative_decode_mla_amd import build
+from tests import asm_hazards
+
+KERNELS = os.path.join(build.HERE, "csrc", "mla_verify_kernels.hip")
+FUNCTIONS = ["_ZN4mlav18mla_verify_partialENS_11PartialArgsE"]
+
+
+@pytest.fixture(scope="module")
+def asm(tmp_path_factory):
+    try:
+        build.hipcc()
+    except RuntimeError:
+        pytest.skip("hipcc not available")
+    out = tmp_path_factory.mktemp("asm") / "kernels.s"
+    build.device_asm(KERNELS, str(out))
+    return out.read_text()
+
+
+@pytest.mark.parametrize("fn", FUNCTIONS)
+def test_no_mfma_hazards(asm, fn):
+    insns, labels = asm_hazards.parse_function(asm, fn)
+    assert sum(asm_hazards.is_mfma(x) for x in insns) >= 68  # the whole main loop was parsed
+    problems = asm_hazards.check(insns, labels)
+    assert not problems, "\n".join(problems[:20])
+
+
+def test_checker_flags_planted_hazards():
+    """The checker itself: each rule fires on a minimal sequence and stays quiet when padded."""
+    def run(text):
+        src = "f:\n" + "\n".join("\t" + l for l in text) + "\n.Lfunc_end0:\n"
+        insns, labels = asm_hazards.parse_function(src, "f")
+        return asm_hazards.check(insns, labels)
+
+    mf = "v_mfma_f32_32x32x16_bf16 v[0:15], v[16:19], v[20:23], v[0:15]"
+    assert run(["v_mov_b32 v17, 0", mf, "s_nop 7", "s_nop 7", "s_nop 7"])      # VALU -> A operand
+    assert not run(["v_mov_b32 v17, 0", "s_nop 3", mf, "s_nop 7", "s_nop 7", "s_nop 7"])
+    assert run([mf, "s_nop 7", "v_add_f32 v30, v3, v4"])                         # result read too early
+    assert not run([mf, "s_nop 7", "s_nop 7", "s_nop 7", "v_add_f32 v30, v3, v4"])
+    assert run([mf, "v_mfma_f32_32x32x16_bf16 v[32:47], v[0:3], v[20:23], v[32:47]", "s_nop 7", "s_nop 7", "s_nop 7"])
+    assert not run([mf, mf, "s_nop 7", "s_nop 7", "s_nop 7"])                   # accumulate chain is fine
+    assert run(["v_exp_f32 v40, v41", "v_cvt_pk_bf16_f32 v42, v40, v43"])       # trans result read at once
+    assert not run(["v_exp_f32 v40, v41", "s_nop 0", "v_cvt_pk_bf16_f32 v42, v40, v43"])
+    # across a branch: the write sits before the label, the MFMA after it
+    assert run(["v_mov_b32 v20, 0", "s_cbranch_scc1 .LBB0_1", "s_nop 0", ".LBB0_1:", mf,
+                "s_nop 7", "s_nop 7", "s_nop 7"])
