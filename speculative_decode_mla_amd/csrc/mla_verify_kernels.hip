@@ -147,8 +147,15 @@ __device__ __forceinline__ int vpack_bf16(float lo, float hi) {  // round to nea
 __device__ __forceinline__ void vadd_to(float& acc, float x) {
   asm volatile("v_add_f32 %0, %0, %1" : "+v"(acc) : "v"(x));
 }
-__device__ __forceinline__ void vsum_pair_to(float& acc, int pair) {  // acc += lo + hi of a bf16 pair
-  asm volatile("v_dot2c_f32_bf16 %0, 0x3f803f80, %1" : "+v"(acc) : "v"(pair));
+// acc += lo + hi of a bf16 pair, widened exactly (a bf16 is the top half of an fp32).
+// Four single-cycle ops: v_dot2c_f32_bf16 would do it in one but holds the wave
+// for about eight cycles next to an MFMA.
+__device__ __forceinline__ void vsum_pair_to(float& acc, int pair) {
+  float lo, hi;
+  asm volatile("v_lshlrev_b32 %0, 16, %1" : "=v"(lo) : "v"(pair));
+  asm volatile("v_and_b32 %0, 0xffff0000, %1" : "=v"(hi) : "v"(pair));
+  asm volatile("v_add_f32 %0, %0, %1" : "+v"(acc) : "v"(lo));
+  asm volatile("v_add_f32 %0, %0, %1" : "+v"(acc) : "v"(hi));
 }
 // 24 wait states: an MFMA result may now be read by VALU / accvgpr moves.
 #define MLAV_MFMA_DRAIN "s_nop 7\n\ts_nop 7\n\ts_nop 7"
@@ -503,6 +510,17 @@ void mla_verify_partial(PartialArgs p) {
     else MLAV_WAIT_VMCNT(0);
     __syncthreads();
   }
+  // V^T fragment n of a tile: local column block n%8, 16-key step n/8.
+  bf16x8 vf[kPvFrags];
+  auto vread = [&](const lds_char* tb, int n) {
+    const int cbl = n & (kHalfColBlocks - 1), kk = n >> 3;
+    const lds_char* vb = tb + (cbl >> 1) * kBlockBytes + kk * 2 * kKeyBlockBytes;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)(vb + vaddr[cbl & 1][0]));
+    const i16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)(vb + vaddr[cbl & 1][1]));
+    vf[n] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
 
   for (int i = 0; i < ntiles; ++i) {
     const int t = wi.t_begin + i;
@@ -558,25 +576,14 @@ void mla_verify_partial(PartialArgs p) {
       ppar[0] = *(const __attribute__((address_space(3))) bf16x8*)(xp);
       ppar[1] = *(const __attribute__((address_space(3))) bf16x8*)(xp + 1024);
     }
-    // V^T fragment n: local column block n%8, 16-key step n/8
-    bf16x8 vf[kPvFrags];
-    auto vread = [&](int n) {
-      const int cbl = n & (kHalfColBlocks - 1), kk = n >> 3;
-      const lds_char* vb = tb + (cbl >> 1) * kBlockBytes + kk * 2 * kKeyBlockBytes;
-      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) i16x4*)(vb + vaddr[cbl & 1][0]));
-      const i16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) i16x4*)(vb + vaddr[cbl & 1][1]));
-      vf[n] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
-    };
     const char* g_row = kv + (int64_t)g_slot * kRowBytes + g_byte;
     const uint32_t g_lds = smem_base + ((i + kAhead) & (kRing - 1)) * kTileBytes + w_uniform * kKeyBlockBytes;
 #pragma unroll
-    for (int n = 0; n < kVPrefetch; ++n) vread(n);
+    for (int n = 0; n < kVPrefetch; ++n) vread(tb, n);
 #pragma unroll
     for (int n = 0; n < kPvFrags; ++n) {
       __builtin_amdgcn_sched_barrier(0);
-      if (n + kVPrefetch < kPvFrags) vread(n + kVPrefetch);
+      if (n + kVPrefetch < kPvFrags) vread(tb, n + kVPrefetch);
       __builtin_amdgcn_sched_barrier(0);
       mfma_acc_a(o_own[n & (kHalfColBlocks - 1)], vf[n], pown[n >> 3]);
       __builtin_amdgcn_sched_barrier(0);
@@ -636,12 +643,20 @@ void mla_verify_partial(PartialArgs p) {
   if (redo != 0) redo_rows_exact(p, wi, row0 + w * kRowsPerWave, (uint32_t)redo);
 }
 
-__global__ __launch_bounds__(256) void mla_verify_merge_kernel(MergeArgs p) {
-  const int lane = threadIdx.x & 63;
-  const int64_t row_global = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+// Kernel 2: one workgroup of 256 threads per (request, row).  Thread t covers
+// output columns 4*(t%128) .. +3 over the splits s = t/128, t/128 + 2, ...; the two
+// halves are added through LDS.  Every thread keeps up to 8 loads of 16 B in
+// flight, so the partials stream at memory speed.  Each wave also forms the
+// merge weights itself: M = max_s lse_s, w_s = exp(lse_s - M) / sum_s exp(lse_s - M).
+constexpr int kMergeThreads = 256;
+constexpr int kMergeUnroll = 8;
+
+__global__ __launch_bounds__(kMergeThreads) void mla_verify_merge_kernel(MergeArgs p) {
+  __shared__ f32x4 half_sum[kMergeThreads / 2];
+  const int tid = threadIdx.x, lane = tid & 63;
   const int rows_per_b = p.max_q_len * p.heads;
-  const int b = (int)(row_global / rows_per_b);
-  const int r = (int)(row_global - (int64_t)b * rows_per_b);
+  const int b = (int)(blockIdx.x / rows_per_b);
+  const int r = (int)(blockIdx.x - (int64_t)b * rows_per_b);
   if (b >= p.batch) return;
   const int Q = clamped_q(p.q_lens, p.seq_lens, b, p.max_q_len);
   if (r >= Q * p.heads) return;
@@ -650,34 +665,47 @@ __global__ __launch_bounds__(256) void mla_verify_merge_kernel(MergeArgs p) {
   for (int i = 0; i < b; ++i) qo += clamped_q(p.q_lens, p.seq_lens, i, p.max_q_len);
 
   const int64_t base = (int64_t)b * p.nsplit * p.rows_stride + r;  // (b, s=0, r)
+  const float* lse_s = p.lse_part + base;
   float M = -INFINITY;
   for (int s0 = 0; s0 < ns; s0 += 64) {
     const int s = s0 + lane;
-    const float v = s < ns ? p.lse_part[base + (int64_t)s * p.rows_stride] : -INFINITY;
-    M = fmaxf(M, wave_max(v));
+    M = fmaxf(M, wave_max(s < ns ? lse_s[(int64_t)s * p.rows_stride] : -INFINITY));
   }
   const float Mref = (M == -INFINITY) ? 0.f : M;
   float Z = 0.f;
   for (int s0 = 0; s0 < ns; s0 += 64) {
     const int s = s0 + lane;
-    const float v = s < ns ? p.lse_part[base + (int64_t)s * p.rows_stride] : -INFINITY;
-    Z += wave_sum(__expf(v - Mref));
+    Z += wave_sum(s < ns ? __expf(lse_s[(int64_t)s * p.rows_stride] - Mref) : 0.f);
   }
   const float invZ = Z > 0.f ? 1.0f / Z : 0.f;
-  f32x4 a0 = {}, a1 = {};
-  for (int s = 0; s < ns; ++s) {
-    const int64_t off = base + (int64_t)s * p.rows_stride;
-    const float ws = __expf(p.lse_part[off] - Mref) * invZ;
-    const f32x4* src = (const f32x4*)(p.o_part + off * kDv) + 2 * lane;
-    a0 += ws * src[0];
-    a1 += ws * src[1];
+
+  const int c4 = tid & (kMergeThreads / 2 - 1), sp = tid >> 7;
+  const float* src = p.o_part + base * kDv + 4 * c4;
+  const int64_t sstride = (int64_t)p.rows_stride * kDv;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = sp; s0 < ns; s0 += 2 * kMergeUnroll) {
+    f32x4 v[kMergeUnroll];
+    float wgt[kMergeUnroll];
+#pragma unroll
+    for (int u = 0; u < kMergeUnroll; ++u) {
+      const int s = s0 + 2 * u;
+      const bool ok = s < ns;
+      v[u] = ok ? *(const f32x4*)(src + (int64_t)s * sstride) : (f32x4){0.f, 0.f, 0.f, 0.f};
+      wgt[u] = ok ? lse_s[(int64_t)s * p.rows_stride] : -INFINITY;
+    }
+#pragma unroll
+    for (int u = 0; u < kMergeUnroll; ++u) acc += (__expf(wgt[u] - Mref) * invZ) * v[u];
   }
-  const int64_t orow = qo * p.heads + r;
-  bf16x8 ov;
-  ov[0] = (__bf16)a0[0]; ov[1] = (__bf16)a0[1]; ov[2] = (__bf16)a0[2]; ov[3] = (__bf16)a0[3];
-  ov[4] = (__bf16)a1[0]; ov[5] = (__bf16)a1[1]; ov[6] = (__bf16)a1[2]; ov[7] = (__bf16)a1[3];
-  *((bf16x8*)(p.out + orow * kDv) + lane) = ov;
-  if (lane == 0) p.lse[orow] = Z > 0.f ? Mref + __logf(Z) : -INFINITY;
+  if (sp == 1) half_sum[c4] = acc;
+  __syncthreads();
+  if (sp == 0) {
+    acc += half_sum[c4];
+    const int64_t orow = qo * p.heads + r;
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    const bf16x4 ov = {(__bf16)acc[0], (__bf16)acc[1], (__bf16)acc[2], (__bf16)acc[3]};
+    *((bf16x4*)(p.out + orow * kDv) + c4) = ov;
+    if (tid == 0) p.lse[orow] = Z > 0.f ? Mref + __logf(Z) : -INFINITY;
+  }
 }
 
 hipError_t launch_partial(const PartialArgs& a, hipStream_t stream) {
@@ -687,9 +715,8 @@ hipError_t launch_partial(const PartialArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream) {
-  const int64_t rows = (int64_t)a.batch * a.max_q_len * a.heads;
-  const int64_t grid = (rows + 3) / 4;
-  hipLaunchKernelGGL(mla_verify_merge_kernel, dim3((unsigned)grid), dim3(256), 0, stream, a);
+  const int64_t rows = (int64_t)a.batch * a.max_q_len * a.heads;  // one workgroup per row
+  hipLaunchKernelGGL(mla_verify_merge_kernel, dim3((unsigned)rows), dim3(kMergeThreads), 0, stream, a);
   return hipGetLastError();
 }
 
