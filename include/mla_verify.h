@@ -73,8 +73,9 @@ typedef struct {
 
 /*
  * Validate `cfg`, allocate the split workspace on the current device
- * (B * max_nsplit * ceil(Q_max*H/128)*128 rows of 512 fp32 plus one fp32
- * log-sum-exp each) and return a handle in *out.  Call outside graph capture.
+ * (B * max_nsplit * ceil(Q_max*H/128)*128 rows of 512 bf16 partial outputs,
+ * each normalised within its split, plus one fp32 log-sum-exp each) and
+ * return a handle in *out.  Call outside graph capture.
  * Errors: INVALID_ARGUMENT (null, non-positive sizes), UNSUPPORTED (dims),
  * OUT_OF_MEMORY, HIP (no device).  On error *out is set to NULL.
  */

@@ -13,7 +13,7 @@ struct mla_verify_s {
   int device;
   int32_t row_groups;
   int32_t rows_pad;
-  float* o_part;    // [B, max_nsplit, rows_pad, 512]
+  uint16_t* o_part;  // bf16 [B, max_nsplit, rows_pad, 512]
   float* lse_part;  // [B, max_nsplit, rows_pad]
 };
 
@@ -69,7 +69,7 @@ int mla_verify_create(const mla_verify_config* cfg, mla_verify_handle* out) {
   h->device = dev;
   h->row_groups = (int32_t)row_groups;
   h->rows_pad = (int32_t)rows_pad;
-  int st = hip_status(hipMalloc((void**)&h->o_part, (size_t)partial_rows * mlav::kDv * sizeof(float)));
+  int st = hip_status(hipMalloc((void**)&h->o_part, (size_t)partial_rows * mlav::kDv * sizeof(uint16_t)));
   if (st == MLA_OK) st = hip_status(hipMalloc((void**)&h->lse_part, (size_t)partial_rows * sizeof(float)));
   if (st != MLA_OK) {
     (void)hipGetLastError();
@@ -150,6 +150,7 @@ int mla_verify_run(mla_verify_handle h, const void* q, const void* kv_pool, cons
   ma.rows_stride = h->rows_pad;
   ma.min_tiles = kMinTilesPerSplit;
   ma.use_all_splits = 0;
+  ma.part_fp32 = 0;
   return mlav::launch_merge(ma, s) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
@@ -176,6 +177,7 @@ int mla_verify_merge(const float* o_part, const float* lse_part, const int32_t* 
   ma.rows_stride = max_q_len * num_heads;
   ma.min_tiles = 1;
   ma.use_all_splits = 1;
+  ma.part_fp32 = 1;
   return hip_status(mlav::launch_merge(ma, static_cast<hipStream_t>(stream))) == MLA_OK ? MLA_OK : MLA_ERR_HIP;
 }
 

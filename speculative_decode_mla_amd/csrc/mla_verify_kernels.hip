@@ -63,9 +63,12 @@ constexpr int kPvFrags = 2 * kHalfColBlocks;       // V^T fragments per wave per
 constexpr int kPrefetch = 6;                       // K fragment reads kept ahead of their MFMA
 constexpr int kVPrefetch = 4;                      // V^T fragment reads kept ahead
 constexpr int kDmaPerTile = 9;                     // direct-to-LDS loads per wave per tile
+constexpr int kStageRowBytes = 528;                // epilogue: one bf16 row half (512 B) + 16 B of padding
+constexpr int kStageBytes = 64 * kStageRowBytes;   // epilogue: one wave's 64 rows
 constexpr float kLn2 = 0.69314718055994530942f;
 static_assert(kTileKeys == 32 && kWaves * 8 == kTileKeys, "one 8-key block per wave per tile");
 static_assert(kRing * kTileBytes + kXchgBytes <= 163840, "LDS budget");
+static_assert(kWaves * kStageBytes <= kRing * kTileBytes, "epilogue staging fits in the ring");
 
 // Number of splits that carry keys for a request of L keys; both kernels use it.
 __device__ __forceinline__ int split_count(int L, int nsplit, int min_tiles) {
@@ -159,6 +162,14 @@ __device__ __forceinline__ void vsum_pair_to(float& acc, int pair) {
 }
 // 24 wait states: an MFMA result may now be read by VALU / accvgpr moves.
 #define MLAV_MFMA_DRAIN "s_nop 7\n\ts_nop 7\n\ts_nop 7"
+
+// One accumulator element out of its AGPR, as a volatile statement so that it keeps its
+// place after the drain (the compiler would otherwise move such reads up to the last MFMA).
+__device__ __forceinline__ float acc_read(float a) {
+  float r;
+  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(r) : "a"(a));
+  return r;
+}
 
 // 16-byte direct-to-LDS load: each lane moves 16 B from gsrc + OFF to LDS at
 // m0 + OFF + 16*lane.  The immediate OFF applies to both addresses, so a caller
@@ -295,9 +306,10 @@ __device__ __forceinline__ void redo_rows_exact(const PartialArgs& p, const Work
     }
     const float inv = l > 0.f ? 1.0f / l : 0.f;
     const int64_t prow = (int64_t)wi.bs * p.rows_pad + row;
-    float* dst = p.o_part + prow * kDv + lane * 8;
+    bf16x8 ov;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) dst[j] = acc[j] * inv;
+    for (int j = 0; j < 8; ++j) ov[j] = (__bf16)(acc[j] * inv);
+    *((bf16x8*)(p.o_part + prow * kDv) + lane) = ov;
     if (lane == 0) p.lse_part[prow] = l > 0.f ? (m + __builtin_amdgcn_logf(l)) * kLn2 : -INFINITY;
   }
 }
@@ -400,11 +412,11 @@ void mla_verify_partial(PartialArgs p) {
   const uint32_t smem_base = (uint32_t)(uintptr_t)smem;
   const int w_uniform = __builtin_amdgcn_readfirstlane(w);
   // Slot index of the row this lane gathers in tile i of the split: key 8w + g_kr of the tile.
-  // Past the request's last key (ragged tail, or refills beyond the split) it is the last
-  // key's row: a valid address whose scores are masked, or a buffer that is never read.
+  // Refills past the split repeat its last tile (still in L2; the buffer is never read), and
+  // keys past the request's end use its last key's row (scores masked).
   const int32_t* slots_g = p.slot_idx + wi.ko;
   auto gather_slot = [&](int i) {
-    int key = (wi.t_begin + i) * kTileKeys + w * 8 + g_kr;
+    int key = (wi.t_begin + (i < ntiles ? i : ntiles - 1)) * kTileKeys + w * 8 + g_kr;
     key = key < L ? key : L - 1;
     return slots_g[key];
   };
@@ -595,64 +607,94 @@ void mla_verify_partial(PartialArgs p) {
     __builtin_amdgcn_sched_barrier(0);
   }
   MLAV_WAIT_VMCNT(0);  // the refills of the last steps (into free buffers) land before the workgroup ends
+  // The accumulators are read below only through acc_read (volatile), which stays behind this drain.
   asm volatile(MLAV_MFMA_DRAIN : "+a"(o_own[kHalfColBlocks - 1]), "+a"(o_par[kHalfColBlocks - 1]));
 
-  // ---- partial write: o_s = O / l, lse_s = ln2 * (m_ref + log2 l) -------------------------------
-  // The row sums live with the row's owner wave; swap them through LDS.
+  // ---- partial write: o_s = O / l (bf16), lse_s = ln2 * (m_ref + log2 l) -----------------------
+  // The row sums live with the row's owner wave; swap them through LDS, together with
+  // whether any row of the workgroup needs the exact redo.
   const float lt = pair_sum(st.l_run);
   const float le = pair_sum(st.l_exact);
-  __syncthreads();  // every wave is done reading the P exchange buffers
-  float* lsum = (float*)(smem_raw + kRing * kTileBytes);
-  if (hi == 0) lsum[w * 32 + lrow] = lt;
-  __syncthreads();
-  const float lt_par = lsum[partner * 32 + lrow];
-  const float inv_own = lt > 0.f ? 1.0f / lt : 0.f;
-  const float inv_par = lt_par > 0.f ? 1.0f / lt_par : 0.f;
-  const int col0 = half * (kDv / 2) + 4 * hi;
-  if (row_valid) {
-    float* dst = p.o_part + ((int64_t)wi.bs * p.rows_pad + myrow) * kDv + col0;
-#pragma unroll
-    for (int c = 0; c < kHalfColBlocks; ++c)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        f32x4 v = {o_own[c][4 * q4] * inv_own, o_own[c][4 * q4 + 1] * inv_own, o_own[c][4 * q4 + 2] * inv_own,
-                   o_own[c][4 * q4 + 3] * inv_own};
-        *(f32x4*)(dst + c * 32 + 8 * q4) = v;
-      }
-    if (hi == 0)
-      p.lse_part[(int64_t)wi.bs * p.rows_pad + myrow] =
-          le > 0.f ? (st.m_ref + __builtin_amdgcn_logf(le)) * kLn2 : -INFINITY;
-  }
-  if (parrow < R) {
-    float* dst = p.o_part + ((int64_t)wi.bs * p.rows_pad + parrow) * kDv + col0;
-#pragma unroll
-    for (int c = 0; c < kHalfColBlocks; ++c)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        f32x4 v = {o_par[c][4 * q4] * inv_par, o_par[c][4 * q4 + 1] * inv_par, o_par[c][4 * q4 + 2] * inv_par,
-                   o_par[c][4 * q4 + 3] * inv_par};
-        *(f32x4*)(dst + c * 32 + 8 * q4) = v;
-      }
-  }
-
-  // Rows whose scores outgrew the fixed reference are redone exactly by their owner
-  // wave, once both halves of the row have been written.
   const bool overflow = !(le < kRowSumLimit);  // some p reached 2^64, or an exp2 overflowed to +inf
   const uint64_t redo = __ballot(overflow && hi == 0 && row_valid);
-  __syncthreads();  // (global writes of both halves are ordered by the barrier's release/acquire)
-  if (redo != 0) redo_rows_exact(p, wi, row0 + w * kRowsPerWave, (uint32_t)redo);
+  __syncthreads();  // every wave is done with the ring and the P exchange buffers
+  float* lsum = (float*)(smem_raw + kRing * kTileBytes);
+  int* redo_flag = (int*)(lsum + kRowsPerGroup);
+  if (hi == 0) lsum[w * 32 + lrow] = lt;
+  if (lane == 0) redo_flag[w] = redo != 0;
+  __syncthreads();
+  const float lt_par = lsum[partner * 32 + lrow];
+  const bool any_redo = (redo_flag[0] | redo_flag[1] | redo_flag[2] | redo_flag[3]) != 0;
+  const float inv_own = lt > 0.f ? 1.0f / lt : 0.f;
+  const float inv_par = lt_par > 0.f ? 1.0f / lt_par : 0.f;
+  if (row_valid && hi == 0)
+    p.lse_part[(int64_t)wi.bs * p.rows_pad + myrow] = le > 0.f ? (st.m_ref + __builtin_amdgcn_logf(le)) * kLn2 : -INFINITY;
+
+  // The wave's 64 rows x 256 columns go through the free ring as bf16 rows (stride
+  // kStageRowBytes, padded against bank conflicts), then out as whole 512-B row halves.
+  // In the C layout the lane holds, per 32-column block c, columns 32c + 8*q4 + 4*hi .. +3.
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  lds_char* stage = smem + w * kStageBytes;
+#pragma unroll
+  for (int c = 0; c < kHalfColBlocks; ++c)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int cb = (32 * c + 8 * q4 + 4 * hi) * 2;
+      const bf16x4 vo = {(__bf16)(acc_read(o_own[c][4 * q4]) * inv_own), (__bf16)(acc_read(o_own[c][4 * q4 + 1]) * inv_own),
+                         (__bf16)(acc_read(o_own[c][4 * q4 + 2]) * inv_own), (__bf16)(acc_read(o_own[c][4 * q4 + 3]) * inv_own)};
+      const bf16x4 vp = {(__bf16)(acc_read(o_par[c][4 * q4]) * inv_par), (__bf16)(acc_read(o_par[c][4 * q4 + 1]) * inv_par),
+                         (__bf16)(acc_read(o_par[c][4 * q4 + 2]) * inv_par), (__bf16)(acc_read(o_par[c][4 * q4 + 3]) * inv_par)};
+      *(__attribute__((address_space(3))) bf16x4*)(stage + lrow * kStageRowBytes + cb) = vo;
+      *(__attribute__((address_space(3))) bf16x4*)(stage + (32 + lrow) * kStageRowBytes + cb) = vp;
+    }
+  // stage rows 0..31 are this wave's rows, 32..63 its partner's; two rows per store instruction
+  uint16_t* part_base = p.o_part + (int64_t)wi.bs * p.rows_pad * kDv + half * (kDv / 2) + (lane & 31) * 8;
+#pragma unroll 4
+  for (int k = 0; k < 32; ++k) {
+    const int r = 2 * k + hi;
+    const i32x4 v = *(const __attribute__((address_space(3))) i32x4*)(stage + r * kStageRowBytes + (lane & 31) * 16);
+    const int grow = row0 + (r < 32 ? w * kRowsPerWave + r : partner * kRowsPerWave + r - 32);
+    if (grow < R) *(i32x4*)(part_base + (int64_t)grow * kDv) = v;
+  }
+
+  // Rows whose sums outgrew the fixed reference are redone exactly by their owner wave,
+  // once both halves of the row have been written.
+  if (any_redo) {
+    __syncthreads();  // (global writes of both halves are ordered by the barrier's release/acquire)
+    if (redo != 0) redo_rows_exact(p, wi, row0 + w * kRowsPerWave, (uint32_t)redo);
+  }
 }
 
 // Kernel 2: one workgroup of 256 threads per (request, row).  Thread t covers
-// output columns 4*(t%128) .. +3 over the splits s = t/128, t/128 + 2, ...; the two
-// halves are added through LDS.  Every thread keeps up to 8 loads of 16 B in
+// output columns 8*(t%64) .. +7 over the splits s = t/64, t/64 + 4, ...; the four
+// partial sums are added through LDS.  Every thread keeps up to 8 loads in
 // flight, so the partials stream at memory speed.  Each wave also forms the
 // merge weights itself: M = max_s lse_s, w_s = exp(lse_s - M) / sum_s exp(lse_s - M).
+// PartT is __bf16 for the library's own workspace, float for caller partials.
 constexpr int kMergeThreads = 256;
+constexpr int kMergeGroups = kMergeThreads / 64;  // split groups
 constexpr int kMergeUnroll = 8;
 
+template <typename PartT>
+__device__ __forceinline__ void load8(const PartT* src, float (&v)[8]);
+template <>
+__device__ __forceinline__ void load8<float>(const float* src, float (&v)[8]) {
+  const f32x4 a = ((const f32x4*)src)[0], b = ((const f32x4*)src)[1];
+  v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3]; v[4] = b[0]; v[5] = b[1]; v[6] = b[2]; v[7] = b[3];
+}
+template <>
+__device__ __forceinline__ void load8<__bf16>(const __bf16* src, float (&v)[8]) {
+  const i32x4 a = *(const i32x4*)src;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    v[2 * j] = __int_as_float(a[j] << 16);
+    v[2 * j + 1] = __int_as_float(a[j] & (int)0xffff0000u);
+  }
+}
+
+template <typename PartT>
 __global__ __launch_bounds__(kMergeThreads) void mla_verify_merge_kernel(MergeArgs p) {
-  __shared__ f32x4 half_sum[kMergeThreads / 2];
+  __shared__ float group_sum[kMergeGroups - 1][64][8];
   const int tid = threadIdx.x, lane = tid & 63;
   const int rows_per_b = p.max_q_len * p.heads;
   const int b = (int)(blockIdx.x / rows_per_b);
@@ -679,31 +721,44 @@ __global__ __launch_bounds__(kMergeThreads) void mla_verify_merge_kernel(MergeAr
   }
   const float invZ = Z > 0.f ? 1.0f / Z : 0.f;
 
-  const int c4 = tid & (kMergeThreads / 2 - 1), sp = tid >> 7;
-  const float* src = p.o_part + base * kDv + 4 * c4;
+  const int c8 = tid & 63, sg = tid >> 6;
+  const PartT* src = (const PartT*)p.o_part + base * kDv + 8 * c8;
   const int64_t sstride = (int64_t)p.rows_stride * kDv;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s0 = sp; s0 < ns; s0 += 2 * kMergeUnroll) {
-    f32x4 v[kMergeUnroll];
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int s0 = sg; s0 < ns; s0 += kMergeGroups * kMergeUnroll) {
+    float v[kMergeUnroll][8];
     float wgt[kMergeUnroll];
 #pragma unroll
     for (int u = 0; u < kMergeUnroll; ++u) {
-      const int s = s0 + 2 * u;
+      const int s = s0 + kMergeGroups * u;
       const bool ok = s < ns;
-      v[u] = ok ? *(const f32x4*)(src + (int64_t)s * sstride) : (f32x4){0.f, 0.f, 0.f, 0.f};
+      if (ok) load8<PartT>(src + (int64_t)s * sstride, v[u]);
+      else
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[u][j] = 0.f;
       wgt[u] = ok ? lse_s[(int64_t)s * p.rows_stride] : -INFINITY;
     }
 #pragma unroll
-    for (int u = 0; u < kMergeUnroll; ++u) acc += (__expf(wgt[u] - Mref) * invZ) * v[u];
+    for (int u = 0; u < kMergeUnroll; ++u) {
+      const float ws = __expf(wgt[u] - Mref) * invZ;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] += ws * v[u][j];
+    }
   }
-  if (sp == 1) half_sum[c4] = acc;
+  if (sg > 0)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) group_sum[sg - 1][c8][j] = acc[j];
   __syncthreads();
-  if (sp == 0) {
-    acc += half_sum[c4];
+  if (sg == 0) {
+#pragma unroll
+    for (int g = 0; g < kMergeGroups - 1; ++g)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] += group_sum[g][c8][j];
     const int64_t orow = qo * p.heads + r;
-    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-    const bf16x4 ov = {(__bf16)acc[0], (__bf16)acc[1], (__bf16)acc[2], (__bf16)acc[3]};
-    *((bf16x4*)(p.out + orow * kDv) + c4) = ov;
+    bf16x8 ov;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ov[j] = (__bf16)acc[j];
+    *((bf16x8*)(p.out + orow * kDv) + c8) = ov;
     if (tid == 0) p.lse[orow] = Z > 0.f ? Mref + __logf(Z) : -INFINITY;
   }
 }
@@ -716,7 +771,10 @@ hipError_t launch_partial(const PartialArgs& a, hipStream_t stream) {
 
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream) {
   const int64_t rows = (int64_t)a.batch * a.max_q_len * a.heads;  // one workgroup per row
-  hipLaunchKernelGGL(mla_verify_merge_kernel, dim3((unsigned)rows), dim3(kMergeThreads), 0, stream, a);
+  if (a.part_fp32)
+    hipLaunchKernelGGL(mla_verify_merge_kernel<float>, dim3((unsigned)rows), dim3(kMergeThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(mla_verify_merge_kernel<__bf16>, dim3((unsigned)rows), dim3(kMergeThreads), 0, stream, a);
   return hipGetLastError();
 }
 
