@@ -425,25 +425,25 @@ void mla_verify_partial(PartialArgs p) {
     dma_key_block(kv + (int64_t)slot * kRowBytes + g_byte, base);
   };
 
-  const int nfirst = min(ntiles, kAhead);
-  {
-    int sl[kAhead];
+  // Slot indices of the first tiles, then the wave's 32 query rows, then the first gathers:
+  // in this order the q loads overlap the wait for the slot indices and the gathers.  The first
+  // kAhead tiles are always gathered (past a short split they repeat its last tile into buffers
+  // that are never read), so the waits below have fixed counts.
+  int sl[kAhead];
 #pragma unroll
-    for (int i = 0; i < kAhead; ++i) sl[i] = gather_slot(i);
-#pragma unroll
-    for (int i = 0; i < kAhead; ++i)
-      if (i < nfirst) issue_tile(i, sl[i]);
-  }
+  for (int i = 0; i < kAhead; ++i) sl[i] = gather_slot(i);
 
   // ---- the wave's 32 query rows, resident for the whole split ----------------------------------
-  // lane holds row lrow, dims 16*ks + 8*hi .. +7 (MFMA B-operand layout)
+  // lane holds row lrow, dims 16*ks + 8*hi .. +7 (MFMA B-operand layout).  A row past the request
+  // reads the request's first row instead: its scores are finite and its output is never stored.
   bf16x8 qf[kQkSteps];
   {
-    const i32x4* qrow = (const i32x4*)(p.q + ((wi.qo * H + (row_valid ? myrow : 0)) * kDqk)) + hi;
-    const int keep = row_valid ? -1 : 0;  // rows past the request are zero
+    const bf16x8* qrow = (const bf16x8*)(p.q + ((wi.qo * H + (row_valid ? myrow : 0)) * kDqk)) + hi;
 #pragma unroll
-    for (int ks = 0; ks < kQkSteps; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, qrow[2 * ks] & keep);
+    for (int ks = 0; ks < kQkSteps; ++ks) qf[ks] = qrow[2 * ks];
   }
+#pragma unroll
+  for (int i = 0; i < kAhead; ++i) issue_tile(i, sl[i]);
 
   // ---- per-lane LDS read addresses (relative to a tile buffer) ---------------------------------
   // Q.K A operand: lane reads key lrow, 16-B chunk 2*ks + hi.
@@ -490,9 +490,8 @@ void mla_verify_partial(PartialArgs p) {
   };
 
   // tile 0 published, Q.K of tile 0; then tile 1 published for the first step
-  if (nfirst == 3) MLAV_WAIT_VMCNT(2 * kDmaPerTile);
-  else if (nfirst == 2) MLAV_WAIT_VMCNT(kDmaPerTile);
-  else MLAV_WAIT_VMCNT(0);
+  static_assert(kAhead == 3, "the waits below count three tiles of gathers");
+  MLAV_WAIT_VMCNT(2 * kDmaPerTile);  // q, the slot indices and tile 0 have arrived
   __syncthreads();
   f32x16 sacc;
 #pragma unroll
@@ -518,8 +517,7 @@ void mla_verify_partial(PartialArgs p) {
     nmref = (st.m_ref == -INFINITY) ? 0.f : -st.m_ref;
   }
   if (ntiles > 1) {
-    if (nfirst == 3) MLAV_WAIT_VMCNT(kDmaPerTile);
-    else MLAV_WAIT_VMCNT(0);
+    MLAV_WAIT_VMCNT(kDmaPerTile);  // tile 1 has arrived
     __syncthreads();
   }
   // V^T fragment n of a tile: local column block n%8, 16-key step n/8.
@@ -675,22 +673,24 @@ constexpr int kMergeThreads = 256;
 constexpr int kMergeGroups = kMergeThreads / 64;  // split groups
 constexpr int kMergeUnroll = 8;
 
+// Eight consecutive partial values: loaded raw (so that a batch of loads is in flight at
+// once), widened to fp32 when used.
 template <typename PartT>
-__device__ __forceinline__ void load8(const PartT* src, float (&v)[8]);
+struct Raw8;
 template <>
-__device__ __forceinline__ void load8<float>(const float* src, float (&v)[8]) {
-  const f32x4 a = ((const f32x4*)src)[0], b = ((const f32x4*)src)[1];
-  v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3]; v[4] = b[0]; v[5] = b[1]; v[6] = b[2]; v[7] = b[3];
-}
+struct Raw8<float> {
+  f32x4 a, b;
+  __device__ void load(const float* src) { a = ((const f32x4*)src)[0]; b = ((const f32x4*)src)[1]; }
+  __device__ float get(int j) const { return j < 4 ? a[j] : b[j - 4]; }
+};
 template <>
-__device__ __forceinline__ void load8<__bf16>(const __bf16* src, float (&v)[8]) {
-  const i32x4 a = *(const i32x4*)src;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    v[2 * j] = __int_as_float(a[j] << 16);
-    v[2 * j + 1] = __int_as_float(a[j] & (int)0xffff0000u);
+struct Raw8<__bf16> {
+  i32x4 a;
+  __device__ void load(const __bf16* src) { a = *(const i32x4*)src; }
+  __device__ float get(int j) const {
+    return (j & 1) ? __int_as_float(a[j >> 1] & (int)0xffff0000u) : __int_as_float(a[j >> 1] << 16);
   }
-}
+};
 
 template <typename PartT>
 __global__ __launch_bounds__(kMergeThreads) void mla_verify_merge_kernel(MergeArgs p) {
@@ -708,42 +708,55 @@ __global__ __launch_bounds__(kMergeThreads) void mla_verify_merge_kernel(MergeAr
 
   const int64_t base = (int64_t)b * p.nsplit * p.rows_stride + r;  // (b, s=0, r)
   const float* lse_s = p.lse_part + base;
-  float M = -INFINITY;
-  for (int s0 = 0; s0 < ns; s0 += 64) {
-    const int s = s0 + lane;
-    M = fmaxf(M, wave_max(s < ns ? lse_s[(int64_t)s * p.rows_stride] : -INFINITY));
-  }
-  const float Mref = (M == -INFINITY) ? 0.f : M;
-  float Z = 0.f;
-  for (int s0 = 0; s0 < ns; s0 += 64) {
-    const int s = s0 + lane;
-    Z += wave_sum(s < ns ? __expf(lse_s[(int64_t)s * p.rows_stride] - Mref) : 0.f);
-  }
-  const float invZ = Z > 0.f ? 1.0f / Z : 0.f;
-
   const int c8 = tid & 63, sg = tid >> 6;
   const PartT* src = (const PartT*)p.o_part + base * kDv + 8 * c8;
   const int64_t sstride = (int64_t)p.rows_stride * kDv;
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int s0 = sg; s0 < ns; s0 += kMergeGroups * kMergeUnroll) {
-    float v[kMergeUnroll][8];
-    float wgt[kMergeUnroll];
+
+  // The LSEs of splits lane, lane + 64, ... go out first, then the first batch of partial
+  // loads; the weights are formed while the partials are in flight.
+  const float x0 = lane < ns ? lse_s[(int64_t)lane * p.rows_stride] : -INFINITY;
+  Raw8<PartT> v[kMergeUnroll];
+  auto load_batch = [&](int s0) {  // splits past ns re-read split 0 (weight 0 below)
 #pragma unroll
     for (int u = 0; u < kMergeUnroll; ++u) {
       const int s = s0 + kMergeGroups * u;
-      const bool ok = s < ns;
-      if (ok) load8<PartT>(src + (int64_t)s * sstride, v[u]);
-      else
-#pragma unroll
-        for (int j = 0; j < 8; ++j) v[u][j] = 0.f;
-      wgt[u] = ok ? lse_s[(int64_t)s * p.rows_stride] : -INFINITY;
+      v[u].load(src + (int64_t)(s < ns ? s : 0) * sstride);
     }
+  };
+  load_batch(sg);
+
+  // M = max_s lse_s and Z = sum_s exp(lse_s - M): per lane (online), then across the wave.
+  float m_l = x0, z_l = x0 > -INFINITY ? 1.f : 0.f;
+  for (int s = lane + 64; s < ns; s += 64) {
+    const float x = lse_s[(int64_t)s * p.rows_stride];
+    const float m_new = fmaxf(m_l, x);
+    if (m_new > -INFINITY) {
+      z_l = z_l * __expf(m_l - m_new) + __expf(x - m_new);
+      m_l = m_new;
+    }
+  }
+  const float M = wave_max(m_l);
+  const float Mref = (M == -INFINITY) ? 0.f : M;
+  const float Z = wave_sum(m_l > -INFINITY ? z_l * __expf(m_l - Mref) : 0.f);
+  const float invZ = Z > 0.f ? 1.0f / Z : 0.f;
+  // weight of split s (wave-uniform): from the lane that loaded its LSE, or from memory past 64 splits
+  auto weight = [&](int s) {
+    const float x = s < 64 ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x0), s))
+                           : lse_s[(int64_t)s * p.rows_stride];
+    return s < ns ? __expf(x - Mref) * invZ : 0.f;
+  };
+
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int s0 = sg;;) {
 #pragma unroll
     for (int u = 0; u < kMergeUnroll; ++u) {
-      const float ws = __expf(wgt[u] - Mref) * invZ;
+      const float ws = weight(s0 + kMergeGroups * u);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc[j] += ws * v[u][j];
+      for (int j = 0; j < 8; ++j) acc[j] += ws * v[u].get(j);
     }
+    s0 += kMergeGroups * kMergeUnroll;
+    if (s0 >= ns) break;
+    load_batch(s0);
   }
   if (sg > 0)
 #pragma unroll
