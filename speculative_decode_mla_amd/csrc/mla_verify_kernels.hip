@@ -116,8 +116,7 @@ __device__ __forceinline__ float pair_sum(float v) {
 // read.  The first does not arise in the schedule below (operands come from LDS
 // reads, which are waited on with lgkmcnt, from the resident q fragments, or
 // from bf16 packs made many instructions earlier); tests/test_kernel_hazards.py
-// checks the generated code for both.  Only the first MFMA of a tile keeps a
-// guard, since it follows the softmax code directly.
+// checks the generated code for both.
 __device__ __forceinline__ void mfma_acc_a(f32x16& acc, const bf16x8& a, const bf16x8& b) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
@@ -125,7 +124,7 @@ __device__ __forceinline__ void mfma_acc_v(f32x16& acc, const bf16x8& a, const b
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
 }
 __device__ __forceinline__ void mfma_first_v(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-  asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(acc) : "v"(a), "v"(b));
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(acc) : "v"(a), "v"(b));
 }
 
 // Single VALU ops as volatile statements, so that each stays in the MFMA gap it
@@ -540,10 +539,17 @@ void mla_verify_partial(PartialArgs p) {
     // loads before the barrier below.  Past the end of the split it is still a valid row,
     // which lands in the free ring buffer and is never read, so the refill needs no branch.
     const int g_slot = gather_slot(i + kAhead);
-    asm volatile(MLAV_MFMA_DRAIN : "+v"(sacc));
+    // (no drain: the last MFMA that wrote sacc is a whole P.V phase back)
     SoftmaxTile sm;
     sm.s = sacc;
     if (t * kTileKeys + kTileKeys > mask_from) mask_tile(sm.s, key0, limit);
+
+    // this wave's P (B-operand layout) for its partner, written as soon as the last pair is packed
+    lds_char* xw = xchg + (i & 1) * (kWaves * 2048) + w * 2048 + lane * 16;
+    auto publish_p = [&]() {
+      *(__attribute__((address_space(3))) i32x4*)(xw) = sm.operand(0);
+      *(__attribute__((address_space(3))) i32x4*)(xw + 1024) = sm.operand(1);
+    };
 
     // ---- phase A: Q.K of tile i+1 with the softmax of tile i between its MFMAs ----
     if (i + 1 < ntiles) {
@@ -560,17 +566,15 @@ void mla_verify_partial(PartialArgs p) {
         else mfma_acc_v(snext, kf[ks], qf[ks]);
         __builtin_amdgcn_sched_barrier(0);
         if (ks < kSoftmaxSlots) softmax_slot(ks, sm, nmref, p.scale_log2);
+        if (ks == kSoftmaxSlots) publish_p();
       }
       __builtin_amdgcn_sched_barrier(0);
       sacc = snext;
     } else {
 #pragma unroll
       for (int slot = 0; slot < kSoftmaxSlots; ++slot) softmax_slot(slot, sm, nmref, p.scale_log2);
+      publish_p();
     }
-    // publish this wave's P (B-operand layout) for its partner
-    lds_char* xw = xchg + (i & 1) * (kWaves * 2048) + w * 2048 + lane * 16;
-    *(__attribute__((address_space(3))) i32x4*)(xw) = sm.operand(0);
-    *(__attribute__((address_space(3))) i32x4*)(xw + 1024) = sm.operand(1);
 
     // tile i+2 complete and every wave's P written, then publish
     MLAV_WAIT_VMCNT(0);
