@@ -339,18 +339,20 @@ __device__ __forceinline__ float tile_row_max(const f32x16& s) {
   return pair_max(m0);
 }
 
-// Softmax of one tile, cut into slices placed between MFMAs.  With one wave per
-// SIMD, an MFMA hides a few independent VALU ops of the same wave but not a
-// long block of them, so the work is spread thin.  The slices that make P sit
-// between the Q.K MFMAs of the next tile (softmax_slot, slot k):
-//   x_k = s_k * scale - m_ref         (one FMA; the scale is folded in here)
-//   p_{k-1} = 2^(x_{k-1})
-//   for k-2 odd: bf16 pack of (p_{k-3}, p_{k-2})   (both made in earlier slots)
+// Softmax of one tile.  First x_k = s_k * scale - m_ref for all 16 scores of the
+// lane (scale_scores, 16 FMAs), issued while the first K reads of the next tile
+// are in flight; they move the scores out of the registers the next tile's Q.K
+// accumulates into, so no copy of them is needed.  Then, with one wave per SIMD
+// an MFMA hides a few independent VALU ops of the same wave but not a long block
+// of them, so the rest is spread thin between the Q.K MFMAs of the next tile
+// (softmax_slot, slot k):
+//   p_k = 2^(x_k)                                   (k < 16)
+//   for even k >= 2: bf16 pack of (p_{k-2}, p_{k-1})  (both made in earlier slots)
 // and the row sums sit between the P.V MFMAs of the same tile (sum_slot):
 //   exact sum += p_n; for odd n, rounded sum += the packed pair.
 // The causal mask is applied to the raw scores beforehand, on the tiles that
 // reach the draft block only.
-constexpr int kSoftmaxSlots = 18;
+constexpr int kSoftmaxSlots = 17;
 struct SoftmaxTile {
   f32x16 s;       // raw scores -> 2^(s*scale - m_ref)
   int pw[8];      // bf16 pairs; pw[0..3], pw[4..7] are the MFMA B operands of the two 16-key steps
@@ -358,10 +360,14 @@ struct SoftmaxTile {
   __device__ i32x4 operand(int kk) const { return (i32x4){pw[4 * kk], pw[4 * kk + 1], pw[4 * kk + 2], pw[4 * kk + 3]}; }
 };
 
-__device__ __forceinline__ void softmax_slot(int k, SoftmaxTile& t, float nmref, float scale_log2) {
-  if (k < 16) t.s[k] = vfma(t.s[k], scale_log2, nmref);
-  if (k >= 1 && k <= 16) t.s[k - 1] = vexp2(t.s[k - 1]);
-  if (k >= 3 && k <= 17 && ((k - 2) & 1)) t.pw[(k - 2) >> 1] = vpack_bf16(t.s[k - 3], t.s[k - 2]);
+__device__ __forceinline__ void scale_scores(SoftmaxTile& t, const f32x16& raw, float nmref, float scale_log2) {
+#pragma unroll
+  for (int k = 0; k < 16; ++k) t.s[k] = vfma(raw[k], scale_log2, nmref);
+}
+
+__device__ __forceinline__ void softmax_slot(int k, SoftmaxTile& t) {
+  if (k < 16) t.s[k] = vexp2(t.s[k]);
+  if (k >= 2 && !(k & 1)) t.pw[(k - 2) >> 1] = vpack_bf16(t.s[k - 2], t.s[k - 1]);
 }
 
 __device__ __forceinline__ void sum_slot(int n, const SoftmaxTile& t, RowSoftmax& st) {
@@ -541,8 +547,7 @@ void mla_verify_partial(PartialArgs p) {
     const int g_slot = gather_slot(i + kAhead);
     // (no drain: the last MFMA that wrote sacc is a whole P.V phase back)
     SoftmaxTile sm;
-    sm.s = sacc;
-    if (t * kTileKeys + kTileKeys > mask_from) mask_tile(sm.s, key0, limit);
+    if (t * kTileKeys + kTileKeys > mask_from) mask_tile(sacc, key0, limit);
 
     // this wave's P (B-operand layout) for its partner, written as soon as the last pair is packed
     lds_char* xw = xchg + (i & 1) * (kWaves * 2048) + w * 2048 + lane * 16;
@@ -557,6 +562,8 @@ void mla_verify_partial(PartialArgs p) {
       f32x16 snext;
 #pragma unroll
       for (int ks = 0; ks < kPrefetch; ++ks) kread(nb, ks);
+      __builtin_amdgcn_sched_barrier(0);
+      scale_scores(sm, sacc, nmref, p.scale_log2);
 #pragma unroll
       for (int ks = 0; ks < kQkSteps; ++ks) {
         __builtin_amdgcn_sched_barrier(0);
@@ -565,14 +572,15 @@ void mla_verify_partial(PartialArgs p) {
         if (ks == 0) mfma_first_v(snext, kf[ks], qf[ks]);
         else mfma_acc_v(snext, kf[ks], qf[ks]);
         __builtin_amdgcn_sched_barrier(0);
-        if (ks < kSoftmaxSlots) softmax_slot(ks, sm, nmref, p.scale_log2);
+        if (ks < kSoftmaxSlots) softmax_slot(ks, sm);
         if (ks == kSoftmaxSlots) publish_p();
       }
       __builtin_amdgcn_sched_barrier(0);
       sacc = snext;
     } else {
+      scale_scores(sm, sacc, nmref, p.scale_log2);
 #pragma unroll
-      for (int slot = 0; slot < kSoftmaxSlots; ++slot) softmax_slot(slot, sm, nmref, p.scale_log2);
+      for (int slot = 0; slot < kSoftmaxSlots; ++slot) softmax_slot(slot, sm);
       publish_p();
     }
 
