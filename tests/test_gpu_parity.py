@@ -68,6 +68,36 @@ def test_ctx4k_workload(api):
     _check(api, I.make_inputs("ctx4k"), 8, "ctx4k")
 
 
+@pytest.mark.parametrize("workload", ["ctx23k", "ctx64k", "ctx91k", "batch16"])
+def test_full_size_sampled_parity(api, workload):
+    """The large workloads at their full sizes and split counts (as the benchmark runs them),
+    checked at sampled (token, head) outputs, which the oracle evaluates one by one: every
+    request's first and last draft token, first and last head, plus seeded random rows."""
+    w = I.WORKLOADS[workload]
+    x = I.make_inputs(workload)
+    d = DeviceInputs(x)
+    h = _handle(api, x, w.nsplit)
+    out, lse = d.run(h, w.nsplit)
+    torch.cuda.synchronize()
+    qo = np.concatenate([[0], np.cumsum(x.q_lens)])
+    rows = []
+    for b in range(len(x.q_lens)):
+        for t in (int(qo[b]), int(qo[b + 1]) - 1):
+            rows += [(t, 0), (t, x.heads - 1)]
+    rng = np.random.default_rng(99)
+    rows += [(int(t), int(hh)) for t, hh in zip(rng.integers(0, x.q.shape[0], 16), rng.integers(0, x.heads, 16))]
+    ref_o, ref_l = oracle.verify_attention_rows(x.q, x.sparse_pool(), x.slot_idx, x.seq_lens, x.q_lens, x.scale, rows)
+    o = bf16_to_f64(out)
+    l = lse.cpu().numpy().astype(np.float64)
+    eo = max(float(np.max(np.abs(o[t, hh] - ref_o[i]))) for i, (t, hh) in enumerate(rows))
+    el = max(abs(float(l[t, hh]) - ref_l[i]) for i, (t, hh) in enumerate(rows))
+    print(f"{workload} nsplit={w.nsplit}, {len(rows)} sampled rows: max|out err|={eo:.3e} max|lse err|={el:.3e}",
+          flush=True)
+    assert eo <= OUT_TOL and el <= LSE_TOL
+    del d, h
+    torch.cuda.empty_cache()
+
+
 def test_single_key_is_exact(api):
     x = I.make_custom(np.random.default_rng(30), [1], [1], 64, 100)
     d = DeviceInputs(x)
