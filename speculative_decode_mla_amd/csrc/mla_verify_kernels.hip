@@ -220,8 +220,41 @@ __device__ __forceinline__ void dma_key_block(const char* row, uint32_t lds_bloc
   dma16<8 * 128>(row, lds_block + 8 * (kBlockBytes - 128));
 }
 
-// s_waitcnt vmcnt(n) with lgkmcnt/expcnt left alone (gfx9 encoding; n < 16).
-#define MLAV_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (0x7 << 4) | (0xF << 8))
+// s_waitcnt vmcnt(n) with lgkmcnt/expcnt left alone.  gfx9 encoding: vmcnt[3:0] in
+// bits 3:0, vmcnt[5:4] in bits 15:14, expcnt in 6:4, lgkmcnt in 11:8.
+#define MLAV_WAIT_VMCNT(n)                                                                   \
+  do {                                                                                       \
+    static_assert((n) >= 0 && (n) < 64, "vmcnt is a 6-bit field");                          \
+    __builtin_amdgcn_s_waitcnt(((n) & 0xF) | ((((n) >> 4) & 0x3) << 14) | (0x7 << 4) | (0xF << 8)); \
+  } while (0)
+
+// Loads whose completion the compiler does not track, for the prologue.  The
+// compiler counts only its own loads in the vmcnt waits it inserts, not the
+// direct-to-LDS loads above, so a compiler-issued q load followed by tile loads
+// would be awaited together with those tiles.  These are awaited explicitly by
+// MLAV_TIE_VMCNT, which names the loaded registers as operands of the wait: every
+// later use reads the wait's output, so none can be placed before it.
+// tests/test_kernel_hazards.py checks the generated code: no instruction touches
+// a register loaded here before a vmcnt wait that covers its load.
+__device__ __forceinline__ int load_b32_untracked(const int32_t* p) {
+  int v;
+  asm volatile("global_load_dword %0, %1, off" : "=v"(v) : "v"(p) : "memory");
+  return v;
+}
+template <int OFF>
+__device__ __forceinline__ bf16x8 load_b128_untracked(const void* p) {
+  bf16x8 v;
+  asm volatile("global_load_dwordx4 %0, %1, off offset:%2" : "=v"(v) : "v"(p), "i"(OFF) : "memory");
+  return v;
+}
+// The wave's 36 q fragments: qf[k] = 16 B at qrow + 32*k bytes.
+template <int K>
+__device__ __forceinline__ void load_q_rows(bf16x8 (&qf)[kQkSteps], const bf16x8* qrow) {
+  qf[K] = load_b128_untracked<32 * K>(qrow);
+  if constexpr (K + 1 < kQkSteps) load_q_rows<K + 1>(qf, qrow);
+}
+// s_waitcnt vmcnt(N) that the listed registers pass through
+#define MLAV_TIE_VMCNT(N, ...) asm volatile("s_waitcnt vmcnt(" #N ")" : __VA_ARGS__)
 
 // bf16 bits -> fp32
 __device__ __forceinline__ float bf16f(uint16_t b) { return __builtin_bit_cast(float, (uint32_t)b << 16); }
@@ -420,35 +453,40 @@ void mla_verify_partial(PartialArgs p) {
   // Refills past the split repeat its last tile (still in L2; the buffer is never read), and
   // keys past the request's end use its last key's row (scores masked).
   const int32_t* slots_g = p.slot_idx + wi.ko;
-  auto gather_slot = [&](int i) {
+  auto gather_key = [&](int i) {
     int key = (wi.t_begin + (i < ntiles ? i : ntiles - 1)) * kTileKeys + w * 8 + g_kr;
-    key = key < L ? key : L - 1;
-    return slots_g[key];
+    return key < L ? key : L - 1;
   };
   auto issue_tile = [&](int buf, int slot) {
     const uint32_t base = smem_base + buf * kTileBytes + w_uniform * kKeyBlockBytes;
     dma_key_block(kv + (int64_t)slot * kRowBytes + g_byte, base);
   };
 
-  // Slot indices of the first tiles, then the wave's 32 query rows, then the first gathers:
-  // in this order the q loads overlap the wait for the slot indices and the gathers.  The first
-  // kAhead tiles are always gathered (past a short split they repeat its last tile into buffers
-  // that are never read), so the waits below have fixed counts.
+  // Slot indices of the first tiles, then the wave's 32 query rows, then the first gathers,
+  // each gather as soon as its slot index has landed: in this order the q loads overlap the
+  // wait for the slot indices and the gathers, and the first Q.K waits for q and tile 0 only.
+  // The first kAhead tiles are always gathered (past a short split they repeat its last tile
+  // into buffers that are never read), so the waits below have fixed counts; all of these
+  // loads are untracked by the compiler and awaited here.
+  static_assert(kAhead == 3, "the waits below count three slot loads and three tiles");
   int sl[kAhead];
 #pragma unroll
-  for (int i = 0; i < kAhead; ++i) sl[i] = gather_slot(i);
+  for (int i = 0; i < kAhead; ++i) sl[i] = load_b32_untracked(slots_g + gather_key(i));
 
   // ---- the wave's 32 query rows, resident for the whole split ----------------------------------
   // lane holds row lrow, dims 16*ks + 8*hi .. +7 (MFMA B-operand layout).  A row past the request
   // reads the request's first row instead: its scores are finite and its output is never stored.
   bf16x8 qf[kQkSteps];
-  {
-    const bf16x8* qrow = (const bf16x8*)(p.q + ((wi.qo * H + (row_valid ? myrow : 0)) * kDqk)) + hi;
-#pragma unroll
-    for (int ks = 0; ks < kQkSteps; ++ks) qf[ks] = qrow[2 * ks];
-  }
-#pragma unroll
-  for (int i = 0; i < kAhead; ++i) issue_tile(i, sl[i]);
+  load_q_rows<0>(qf, (const bf16x8*)(p.q + ((wi.qo * H + (row_valid ? myrow : 0)) * kDqk)) + hi);
+
+  // loads issued after slot i: the later slots, the q rows, the gathers of tiles < i
+  static_assert(38 == 2 + kQkSteps && 46 == 1 + kQkSteps + kDmaPerTile && 54 == kQkSteps + 2 * kDmaPerTile, "");
+  MLAV_TIE_VMCNT(38, "+v"(sl[0]));
+  issue_tile(0, sl[0]);
+  MLAV_TIE_VMCNT(46, "+v"(sl[1]));
+  issue_tile(1, sl[1]);
+  MLAV_TIE_VMCNT(54, "+v"(sl[2]));
+  issue_tile(2, sl[2]);
 
   // ---- per-lane LDS read addresses (relative to a tile buffer) ---------------------------------
   // Q.K A operand: lane reads key lrow, 16-B chunk 2*ks + hi.
@@ -495,8 +533,14 @@ void mla_verify_partial(PartialArgs p) {
   };
 
   // tile 0 published, Q.K of tile 0; then tile 1 published for the first step
-  static_assert(kAhead == 3, "the waits below count three tiles of gathers");
-  MLAV_WAIT_VMCNT(2 * kDmaPerTile);  // q, the slot indices and tile 0 have arrived
+  // q and tile 0 have arrived: only the gathers of tiles 1 and 2 may be in flight
+  static_assert(18 == 2 * kDmaPerTile, "");
+  MLAV_TIE_VMCNT(18, "+v"(qf[0]), "+v"(qf[1]), "+v"(qf[2]), "+v"(qf[3]), "+v"(qf[4]), "+v"(qf[5]),
+                 "+v"(qf[6]), "+v"(qf[7]), "+v"(qf[8]), "+v"(qf[9]), "+v"(qf[10]), "+v"(qf[11]));
+  asm volatile("" : "+v"(qf[12]), "+v"(qf[13]), "+v"(qf[14]), "+v"(qf[15]), "+v"(qf[16]), "+v"(qf[17]),
+               "+v"(qf[18]), "+v"(qf[19]), "+v"(qf[20]), "+v"(qf[21]), "+v"(qf[22]), "+v"(qf[23]));
+  asm volatile("" : "+v"(qf[24]), "+v"(qf[25]), "+v"(qf[26]), "+v"(qf[27]), "+v"(qf[28]), "+v"(qf[29]),
+               "+v"(qf[30]), "+v"(qf[31]), "+v"(qf[32]), "+v"(qf[33]), "+v"(qf[34]), "+v"(qf[35]));
   __syncthreads();
   f32x16 sacc;
 #pragma unroll
@@ -544,7 +588,7 @@ void mla_verify_partial(PartialArgs p) {
     // Slot of the row this lane gathers for tile i+3, loaded now and awaited with the tile
     // loads before the barrier below.  Past the end of the split it is still a valid row,
     // which lands in the free ring buffer and is never read, so the refill needs no branch.
-    const int g_slot = gather_slot(i + kAhead);
+    const int g_slot = slots_g[gather_key(i + kAhead)];
     // (no drain: the last MFMA that wrote sacc is a whole P.V phase back)
     SoftmaxTile sm;
     if (t * kTileKeys + kTileKeys > mask_from) mask_tile(sacc, key0, limit);
@@ -617,8 +661,10 @@ void mla_verify_partial(PartialArgs p) {
     __builtin_amdgcn_sched_barrier(0);
   }
   MLAV_WAIT_VMCNT(0);  // the refills of the last steps (into free buffers) land before the workgroup ends
-  // The accumulators are read below only through acc_read (volatile), which stays behind this drain.
-  asm volatile(MLAV_MFMA_DRAIN : "+a"(o_own[kHalfColBlocks - 1]), "+a"(o_par[kHalfColBlocks - 1]));
+  // The accumulators are read below only through acc_read (volatile), which stays behind this
+  // drain.  It names no registers: tied operands here made the compiler move accumulators
+  // between registers ahead of it.
+  asm volatile(MLAV_MFMA_DRAIN);
 
   // ---- partial write: o_s = O / l (bf16), lse_s = ln2 * (m_ref + log2 l) -----------------------
   // The row sums live with the row's owner wave; swap them through LDS, together with

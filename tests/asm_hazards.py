@@ -18,6 +18,11 @@ kernels use):
     writes a register -> a non-transcendental VALU op reads it: 1 (as the ISA asks;
     the compiler itself inserts exactly this many).
 
+`check_untracked_loads` covers the vector memory loads issued through inline
+asm (the compiler does not count them in the vmcnt waits it inserts): from such
+a load until an `s_waitcnt vmcnt(N)` with at least N vector memory operations
+issued after it, no instruction may read or write its destination registers.
+
 Every instruction provides one wait state and `s_nop N` provides N + 1.  Control
 flow is followed both ways: a label's predecessors are the fall-through and
 every branch to it; a conditional branch continues to its target and falls
@@ -42,6 +47,7 @@ class Insn:
     op: str
     operands: list
     text: str
+    inline_asm: bool = False  # between the compiler's ASMSTART / ASMEND markers
 
 
 def _regs(tok):
@@ -69,7 +75,13 @@ def parse_function(asm: str, name: str):
     lines = asm.splitlines()
     start = next(i for i, l in enumerate(lines) if l.startswith(name + ":"))
     insns, labels = [], {}
+    in_asm = False
     for l in lines[start + 1:]:
+        raw = l.strip()
+        if raw.startswith(";;#ASMSTART"):
+            in_asm = True
+        elif raw.startswith(";;#ASMEND"):
+            in_asm = False
         s = l.split(";")[0].split("//")[0].strip()
         if s.startswith(".Lfunc_end"):
             break
@@ -83,7 +95,7 @@ def parse_function(asm: str, name: str):
         parts = s.split(None, 1)
         op = parts[0]
         ops = _split_operands(parts[1]) if len(parts) > 1 else []
-        insns.append(Insn(len(insns), op, ops, s))
+        insns.append(Insn(len(insns), op, ops, s, in_asm))
     return insns, labels
 
 
@@ -220,3 +232,42 @@ def check(insns, labels):
             return True
         _walk(succ[tr.idx], lambda i: succ[i], TRANS_RESULT, tfwd)
     return sorted(set(problems))
+
+
+_VMEM = ("global_load", "global_store", "global_atomic", "buffer_load", "buffer_store", "buffer_atomic",
+         "flat_load", "flat_store", "flat_atomic", "scratch_load", "scratch_store")
+_VMCNT = re.compile(r"vmcnt\((\d+)\)")
+
+
+def _is_vmem(insn):
+    return insn.op.startswith(_VMEM)
+
+
+def check_untracked_loads(insns):
+    """Reports for inline-asm vector loads whose registers are used before a covering wait.
+
+    Straight-line code is required between such a load and its wait: a branch in
+    between is reported as well.
+    """
+    problems = []
+    for ld in insns:
+        if not (ld.inline_asm and ld.op.startswith(("global_load", "buffer_load")) and "lds" not in ld.op):
+            continue
+        dst = {r for r in _regs(ld.operands[0]) if r[0] in "va"}
+        newer = 0
+        for x in insns[ld.idx + 1:]:
+            if x.op == "s_waitcnt":
+                m = _VMCNT.search(x.text)
+                if m and newer >= int(m.group(1)):
+                    break
+                continue
+            if _is_branch(x) or _ends_flow(x):
+                problems.append(f"'{ld.text}': control flow '{x.text}' before its wait")
+                break
+            if _all_regs(x) & dst:
+                problems.append(f"'{ld.text}': '{x.text}' uses its registers before its wait")
+            if _is_vmem(x):
+                newer += 1
+        else:
+            problems.append(f"'{ld.text}': never awaited")
+    return problems

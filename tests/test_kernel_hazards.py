@@ -32,6 +32,32 @@ def test_no_mfma_hazards(asm, fn):
     assert not problems, "\n".join(problems[:20])
 
 
+@pytest.mark.parametrize("fn", FUNCTIONS)
+def test_untracked_loads_awaited_before_use(asm, fn):
+    insns, _ = asm_hazards.parse_function(asm, fn)
+    loads = [x for x in insns if x.inline_asm and x.op.startswith("global_load_dword")]
+    assert len(loads) >= 3 + 36  # the prologue's slot indices and q fragments were found
+    problems = asm_hazards.check_untracked_loads(insns)
+    assert not problems, "\n".join(problems[:20])
+
+
+def test_untracked_load_checker_flags_early_use():
+    def run(text):
+        src = "f:\n" + "\n".join("\t" + l for l in text) + "\n.Lfunc_end0:\n"
+        insns, _ = asm_hazards.parse_function(src, "f")
+        return asm_hazards.check_untracked_loads(insns)
+
+    ld = [";;#ASMSTART", "global_load_dwordx4 v[4:7], v[0:1], off", ";;#ASMEND"]
+    other = "global_load_dword v8, v[2:3], off"
+    assert not run(ld + [other, "s_waitcnt vmcnt(1)", "v_mov_b32 v9, v5", "s_endpgm"])
+    assert run(ld + [other, "s_waitcnt vmcnt(2)", "v_mov_b32 v9, v5", "s_waitcnt vmcnt(0)", "s_endpgm"])
+    assert run(ld + ["v_mov_b32 v9, v6", "s_waitcnt vmcnt(0)", "s_endpgm"])     # read before the wait
+    assert run(ld + ["v_mov_b32 v7, 0", "s_waitcnt vmcnt(0)", "s_endpgm"])      # overwritten before the wait
+    assert run(ld + ["s_cbranch_scc1 .LBB0_1", ".LBB0_1:", "s_waitcnt vmcnt(0)", "s_endpgm"])
+    assert run(ld + ["s_endpgm"])                                                # never awaited
+    assert not run(["global_load_dwordx4 v[4:7], v[0:1], off", "v_mov_b32 v9, v5"])  # compiler-issued: not checked
+
+
 def test_checker_flags_planted_hazards():
     """The checker itself: each rule fires on a minimal sequence and stays quiet when padded."""
     def run(text):
