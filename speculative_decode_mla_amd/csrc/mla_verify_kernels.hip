@@ -228,33 +228,18 @@ __device__ __forceinline__ void dma_key_block(const char* row, uint32_t lds_bloc
     __builtin_amdgcn_s_waitcnt(((n) & 0xF) | ((((n) >> 4) & 0x3) << 14) | (0x7 << 4) | (0xF << 8)); \
   } while (0)
 
-// Loads whose completion the compiler does not track, for the prologue.  The
-// compiler counts only its own loads in the vmcnt waits it inserts, not the
-// direct-to-LDS loads above, so a compiler-issued q load followed by tile loads
-// would be awaited together with those tiles.  These are awaited explicitly by
-// MLAV_TIE_VMCNT, which names the loaded registers as operands of the wait: every
-// later use reads the wait's output, so none can be placed before it.
-// tests/test_kernel_hazards.py checks the generated code: no instruction touches
-// a register loaded here before a vmcnt wait that covers its load.
+// A load whose completion the compiler does not track (the prologue's slot indices).  The
+// compiler counts only its own loads in the vmcnt waits it inserts, not the direct-to-LDS loads
+// above, so a compiler-issued load followed by gathers would be awaited together with them.
+// The loaded register is awaited explicitly by an asm s_waitcnt that names it as an in/out
+// operand: every later use reads the wait's output, so none can be placed before it.
+// tests/test_kernel_hazards.py checks the generated code: no instruction touches a register
+// loaded here before a vmcnt wait that covers its load.
 __device__ __forceinline__ int load_b32_untracked(const int32_t* p) {
   int v;
   asm volatile("global_load_dword %0, %1, off" : "=v"(v) : "v"(p) : "memory");
   return v;
 }
-template <int OFF>
-__device__ __forceinline__ bf16x8 load_b128_untracked(const void* p) {
-  bf16x8 v;
-  asm volatile("global_load_dwordx4 %0, %1, off offset:%2" : "=v"(v) : "v"(p), "i"(OFF) : "memory");
-  return v;
-}
-// The wave's 36 q fragments: qf[k] = 16 B at qrow + 32*k bytes.
-template <int K>
-__device__ __forceinline__ void load_q_rows(bf16x8 (&qf)[kQkSteps], const bf16x8* qrow) {
-  qf[K] = load_b128_untracked<32 * K>(qrow);
-  if constexpr (K + 1 < kQkSteps) load_q_rows<K + 1>(qf, qrow);
-}
-// s_waitcnt vmcnt(N) that the listed registers pass through
-#define MLAV_TIE_VMCNT(N, ...) asm volatile("s_waitcnt vmcnt(" #N ")" : __VA_ARGS__)
 
 // bf16 bits -> fp32
 __device__ __forceinline__ float bf16f(uint16_t b) { return __builtin_bit_cast(float, (uint32_t)b << 16); }
@@ -462,34 +447,7 @@ void mla_verify_partial(PartialArgs p) {
     dma_key_block(kv + (int64_t)slot * kRowBytes + g_byte, base);
   };
 
-  // Slot indices of the first tiles, then the wave's 32 query rows, then the first gathers,
-  // each gather as soon as its slot index has landed: in this order the q loads overlap the
-  // wait for the slot indices and the gathers, and the first Q.K waits for q and tile 0 only.
-  // The first kAhead tiles are always gathered (past a short split they repeat its last tile
-  // into buffers that are never read), so the waits below have fixed counts; all of these
-  // loads are untracked by the compiler and awaited here.
-  static_assert(kAhead == 3, "the waits below count three slot loads and three tiles");
-  int sl[kAhead];
-#pragma unroll
-  for (int i = 0; i < kAhead; ++i) sl[i] = load_b32_untracked(slots_g + gather_key(i));
-
-  // ---- the wave's 32 query rows, resident for the whole split ----------------------------------
-  // lane holds row lrow, dims 16*ks + 8*hi .. +7 (MFMA B-operand layout).  A row past the request
-  // reads the request's first row instead: its scores are finite and its output is never stored.
-  bf16x8 qf[kQkSteps];
-  load_q_rows<0>(qf, (const bf16x8*)(p.q + ((wi.qo * H + (row_valid ? myrow : 0)) * kDqk)) + hi);
-
-  // loads issued after slot i: the later slots, the q rows, the gathers of tiles < i
-  static_assert(38 == 2 + kQkSteps && 46 == 1 + kQkSteps + kDmaPerTile && 54 == kQkSteps + 2 * kDmaPerTile, "");
-  MLAV_TIE_VMCNT(38, "+v"(sl[0]));
-  issue_tile(0, sl[0]);
-  MLAV_TIE_VMCNT(46, "+v"(sl[1]));
-  issue_tile(1, sl[1]);
-  MLAV_TIE_VMCNT(54, "+v"(sl[2]));
-  issue_tile(2, sl[2]);
-
-  // ---- per-lane LDS read addresses (relative to a tile buffer) ---------------------------------
-  // Q.K A operand: lane reads key lrow, 16-B chunk 2*ks + hi.
+  // Q.K A operand: lane reads key lrow, 16-B chunk 2*ks + hi (relative to a tile buffer).
   int kaddr[4];
   {
     const int kr = lrow & 7, f = kr ^ ((lrow >> 3) & 1);
@@ -497,6 +455,48 @@ void mla_verify_partial(PartialArgs p) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) kaddr[j] = base + (((2 * j) ^ hi ^ f) << 4);
   }
+
+  // ---- prologue: slot indices, the q rows, then the first gathers --------------------------------
+  // The slot indices of the first kAhead tiles are loaded first (untracked by the compiler,
+  // awaited below).  The first kAhead tiles are always gathered (past a short split they repeat
+  // its last tile into buffers that are never read), so the waits have fixed counts.
+  static_assert(kAhead == 3, "the prologue loads three slot indices and gathers three tiles");
+  int sl[kAhead];
+#pragma unroll
+  for (int i = 0; i < kAhead; ++i) sl[i] = load_b32_untracked(slots_g + gather_key(i));
+
+  // The wave's 32 query rows, resident in registers for the whole split: lane holds row lrow,
+  // dims 16*ks + 8*hi .. +7 (MFMA B-operand layout).  Loads straight into that layout would make
+  // every load touch 32 rows (32 partial 128-B lines), which costs microseconds of address
+  // processing per workgroup; so wave w moves its rows into ring buffer w in the key-tile layout
+  // (row r of the wave as key r; 8 whole lines per load) and reads them back with the Q.K read
+  // pattern.  A row past the request reads the request's first row instead: its scores are finite
+  // and its output is never stored.
+  {
+    const uint32_t qbuf = smem_base + w_uniform * kTileBytes;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const int r = row0 + w * kRowsPerWave + 8 * kb + g_kr;
+      const int64_t qrow = wi.qo * H + (r < R ? r : 0);
+      dma_key_block((const char*)(p.q + qrow * kDqk) + (((lane & 7) ^ g_kr ^ (kb & 1)) << 4), qbuf + kb * kKeyBlockBytes);
+    }
+  }
+  // slot indices and q rows have landed; the memory clobber keeps the LDS reads below after it
+  asm volatile("s_waitcnt vmcnt(0)" : "+v"(sl[0]), "+v"(sl[1]), "+v"(sl[2]) : : "memory");
+  bf16x8 qf[kQkSteps];
+  {
+    const lds_char* qb = smem + w * kTileBytes;
+#pragma unroll
+    for (int ks = 0; ks < kQkSteps; ++ks)
+      qf[ks] = *(const __attribute__((address_space(3))) bf16x8*)(qb + kaddr[ks & 3] + (ks >> 2) * kBlockBytes);
+  }
+  // every wave holds its q before the ring is refilled with tiles
+  asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kAhead; ++i) issue_tile(i, sl[i]);
+
+  // ---- per-lane LDS read addresses for P.V (relative to a tile buffer) --------------------------
   // P.V A operand via the 4x16 transposing read: in 16-lane group G, lane j reads key
   // 16*kk + 8*r + 4*(G>>1) + (j>>2) at columns 32*cb + 16*(G&1) + 4*(j&3) .. +3; lane l then
   // holds column 32*cb + (l&31) for keys 16*kk + 8*r + 4*(l>>5) .. +3.  This wave's column
@@ -533,14 +533,8 @@ void mla_verify_partial(PartialArgs p) {
   };
 
   // tile 0 published, Q.K of tile 0; then tile 1 published for the first step
-  // q and tile 0 have arrived: only the gathers of tiles 1 and 2 may be in flight
   static_assert(18 == 2 * kDmaPerTile, "");
-  MLAV_TIE_VMCNT(18, "+v"(qf[0]), "+v"(qf[1]), "+v"(qf[2]), "+v"(qf[3]), "+v"(qf[4]), "+v"(qf[5]),
-                 "+v"(qf[6]), "+v"(qf[7]), "+v"(qf[8]), "+v"(qf[9]), "+v"(qf[10]), "+v"(qf[11]));
-  asm volatile("" : "+v"(qf[12]), "+v"(qf[13]), "+v"(qf[14]), "+v"(qf[15]), "+v"(qf[16]), "+v"(qf[17]),
-               "+v"(qf[18]), "+v"(qf[19]), "+v"(qf[20]), "+v"(qf[21]), "+v"(qf[22]), "+v"(qf[23]));
-  asm volatile("" : "+v"(qf[24]), "+v"(qf[25]), "+v"(qf[26]), "+v"(qf[27]), "+v"(qf[28]), "+v"(qf[29]),
-               "+v"(qf[30]), "+v"(qf[31]), "+v"(qf[32]), "+v"(qf[33]), "+v"(qf[34]), "+v"(qf[35]));
+  MLAV_WAIT_VMCNT(18);  // tile 0 has arrived: only the gathers of tiles 1 and 2 may be in flight
   __syncthreads();
   f32x16 sacc;
 #pragma unroll

@@ -36,7 +36,7 @@ def test_no_mfma_hazards(asm, fn):
 def test_untracked_loads_awaited_before_use(asm, fn):
     insns, _ = asm_hazards.parse_function(asm, fn)
     loads = [x for x in insns if x.inline_asm and x.op.startswith("global_load_dword")]
-    assert len(loads) >= 3 + 36  # the prologue's slot indices and q fragments were found
+    assert len(loads) >= 3  # the prologue's slot indices were found
     problems = asm_hazards.check_untracked_loads(insns)
     assert not problems, "\n".join(problems[:20])
 
