@@ -37,6 +37,8 @@
 //     across each 16-lane group.  Waves 2k and 2k+1 form a pair: each computes
 //     256 of the 512 output columns for the pair's 64 rows, taking its
 //     partner's P through LDS, so each wave reads only half of V.
+#include <type_traits>
+
 #include "mla_verify_internal.h"
 
 namespace mlav {
@@ -435,8 +437,8 @@ void mla_verify_partial(PartialArgs p) {
   const uint32_t smem_base = (uint32_t)(uintptr_t)smem;
   const int w_uniform = __builtin_amdgcn_readfirstlane(w);
   // Slot index of the row this lane gathers in tile i of the split: key 8w + g_kr of the tile.
-  // Refills past the split repeat its last tile (still in L2; the buffer is never read), and
-  // keys past the request's end use its last key's row (scores masked).
+  // The prologue's gathers past a short split repeat its last tile (the buffer is never read),
+  // and keys past the request's end use its last key's row (scores masked).
   const int32_t* slots_g = p.slot_idx + wi.ko;
   auto gather_key = [&](int i) {
     int key = (wi.t_begin + (i < ntiles ? i : ntiles - 1)) * kTileKeys + w * 8 + g_kr;
@@ -575,14 +577,17 @@ void mla_verify_partial(PartialArgs p) {
     vf[n] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
   };
 
-  for (int i = 0; i < ntiles; ++i) {
+  // One step; `refill` (a compile-time flag) says whether it gathers tile i+3, which the
+  // last kAhead steps of a split do not: the loop runs in two parts, each with its own copy
+  // of the step, so there is no branch inside a step.
+  auto step = [&](const int i, auto refill) __attribute__((always_inline)) {
+    constexpr bool kRefill = decltype(refill)::value;
     const int t = wi.t_begin + i;
     const lds_char* tb = smem + (i & (kRing - 1)) * kTileBytes;
     const int key0 = t * kTileKeys + 4 * hi;
     // Slot of the row this lane gathers for tile i+3, loaded now and awaited with the tile
-    // loads before the barrier below.  Past the end of the split it is still a valid row,
-    // which lands in the free ring buffer and is never read, so the refill needs no branch.
-    const int g_slot = slots_g[gather_key(i + kAhead)];
+    // loads before the barrier below.
+    const int g_slot = kRefill ? slots_g[gather_key(i + kAhead)] : 0;
     // (no drain: the last MFMA that wrote sacc is a whole P.V phase back)
     SoftmaxTile sm;
     if (t * kTileKeys + kTileKeys > mask_from) mask_tile(sacc, key0, limit);
@@ -648,13 +653,16 @@ void mla_verify_partial(PartialArgs p) {
       mfma_acc_a(o_own[n & (kHalfColBlocks - 1)], vf[n], pown[n >> 3]);
       __builtin_amdgcn_sched_barrier(0);
       sum_slot(n, sm, st);
-      if (n < kDmaPerTile) dma_chunk_group(g_row, g_lds, n);
+      if (kRefill && n < kDmaPerTile) dma_chunk_group(g_row, g_lds, n);
       __builtin_amdgcn_sched_barrier(0);
       mfma_acc_a(o_par[n & (kHalfColBlocks - 1)], vf[n], ppar[n >> 3]);
     }
     __builtin_amdgcn_sched_barrier(0);
-  }
-  MLAV_WAIT_VMCNT(0);  // the refills of the last steps (into free buffers) land before the workgroup ends
+  };
+  int i = 0;
+  for (; i < ntiles - kAhead; ++i) step(i, std::true_type{});
+  for (; i < ntiles; ++i) step(i, std::false_type{});
+  MLAV_WAIT_VMCNT(0);
   // The accumulators are read below only through acc_read (volatile), which stays behind this
   // drain.  It names no registers: tied operands here made the compiler move accumulators
   // between registers ahead of it.
