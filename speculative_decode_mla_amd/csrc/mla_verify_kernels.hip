@@ -492,11 +492,12 @@ void mla_verify_partial(PartialArgs p) {
     for (int ks = 0; ks < kQkSteps; ++ks)
       qf[ks] = *(const __attribute__((address_space(3))) bf16x8*)(qb + kaddr[ks & 3] + (ks >> 2) * kBlockBytes);
   }
-  // every wave holds its q before the ring is refilled with tiles
+  // every wave holds its q before the ring is refilled with tiles; tile 0 first, tiles 1 and 2
+  // between the Q.K MFMAs of tile 0 (each gather load takes the address unit for a while, so
+  // issuing all three here would delay the first Q.K)
   asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
   __syncthreads();
-#pragma unroll
-  for (int i = 0; i < kAhead; ++i) issue_tile(i, sl[i]);
+  issue_tile(0, sl[0]);
 
   // ---- per-lane LDS read addresses for P.V (relative to a tile buffer) --------------------------
   // P.V A operand via the 4x16 transposing read: in 16-lane group G, lane j reads key
@@ -534,10 +535,15 @@ void mla_verify_partial(PartialArgs p) {
     kf[ks] = *(const __attribute__((address_space(3))) bf16x8*)(tb + kaddr[ks & 3] + (ks >> 2) * kBlockBytes);
   };
 
-  // tile 0 published, Q.K of tile 0; then tile 1 published for the first step
-  static_assert(18 == 2 * kDmaPerTile, "");
-  MLAV_WAIT_VMCNT(18);  // tile 0 has arrived: only the gathers of tiles 1 and 2 may be in flight
+  // tile 0 published, Q.K of tile 0 with the gathers of tiles 1 and 2 between its MFMAs; then
+  // tile 1 published for the first step
+  MLAV_WAIT_VMCNT(0);  // tile 0 has arrived (nothing else is in flight)
   __syncthreads();
+  const char* g_row1 = kv + (int64_t)sl[1] * kRowBytes + g_byte;
+  const char* g_row2 = kv + (int64_t)sl[2] * kRowBytes + g_byte;
+  const uint32_t g_lds1 = smem_base + 1 * kTileBytes + w_uniform * kKeyBlockBytes;
+  const uint32_t g_lds2 = smem_base + 2 * kTileBytes + w_uniform * kKeyBlockBytes;
+  static_assert(2 * 2 * kDmaPerTile <= kQkSteps, "two tiles of gathers fit in one Q.K, one per two MFMAs");
   f32x16 sacc;
 #pragma unroll
   for (int ks = 0; ks < kPrefetch; ++ks) kread(smem, ks);
@@ -548,6 +554,12 @@ void mla_verify_partial(PartialArgs p) {
     __builtin_amdgcn_sched_barrier(0);
     if (ks == 0) mfma_first_v(sacc, kf[ks], qf[ks]);
     else mfma_acc_v(sacc, kf[ks], qf[ks]);
+    __builtin_amdgcn_sched_barrier(0);
+    if (!(ks & 1) && (ks >> 1) < 2 * kDmaPerTile) {
+      const int j = ks >> 1;
+      if (j < kDmaPerTile) dma_chunk_group(g_row1, g_lds1, j);
+      else dma_chunk_group(g_row2, g_lds2, j - kDmaPerTile);
+    }
   }
   __builtin_amdgcn_sched_barrier(0);
   // The reference: the first tile's row max (masked).  If the row sees no key of
