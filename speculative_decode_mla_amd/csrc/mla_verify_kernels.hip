@@ -577,6 +577,9 @@ void mla_verify_partial(PartialArgs p) {
     MLAV_WAIT_VMCNT(kDmaPerTile);  // tile 1 has arrived
     __syncthreads();
   }
+  // the first K fragments of tile 1 for the first step's Q.K (unused when there is no tile 1)
+#pragma unroll
+  for (int ks = 0; ks < kPrefetch; ++ks) kread(smem + kTileBytes, ks);
   // V^T fragment n of a tile: local column block n%8, 16-key step n/8.
   bf16x8 vf[kPvFrags];
   auto vread = [&](const lds_char* tb, int n) {
@@ -615,14 +618,15 @@ void mla_verify_partial(PartialArgs p) {
     if (i + 1 < ntiles) {
       const lds_char* nb = smem + ((i + 1) & (kRing - 1)) * kTileBytes;
       f32x16 snext;
-#pragma unroll
-      for (int ks = 0; ks < kPrefetch; ++ks) kread(nb, ks);
+      // kf[0 .. kPrefetch) of this tile were read during the previous P.V phase
       __builtin_amdgcn_sched_barrier(0);
       scale_scores(sm, sacc, nmref, p.scale_log2);
 #pragma unroll
       for (int ks = 0; ks < kQkSteps; ++ks) {
         __builtin_amdgcn_sched_barrier(0);
         if (ks + kPrefetch < kQkSteps) kread(nb, ks + kPrefetch);
+        // the first V^T fragments of tile i, for the P.V phase after the barrier
+        if (ks >= kQkSteps - kVPrefetch) vread(tb, ks - (kQkSteps - kVPrefetch));
         __builtin_amdgcn_sched_barrier(0);
         if (ks == 0) mfma_first_v(snext, kf[ks], qf[ks]);
         else mfma_acc_v(snext, kf[ks], qf[ks]);
@@ -637,6 +641,8 @@ void mla_verify_partial(PartialArgs p) {
 #pragma unroll
       for (int slot = 0; slot < kSoftmaxSlots; ++slot) softmax_slot(slot, sm);
       publish_p();
+#pragma unroll
+      for (int n = 0; n < kVPrefetch; ++n) vread(tb, n);
     }
 
     // tile i+2 complete and every wave's P written, then publish
@@ -655,12 +661,14 @@ void mla_verify_partial(PartialArgs p) {
     }
     const char* g_row = kv + (int64_t)g_slot * kRowBytes + g_byte;
     const uint32_t g_lds = smem_base + ((i + kAhead) & (kRing - 1)) * kTileBytes + w_uniform * kKeyBlockBytes;
-#pragma unroll
-    for (int n = 0; n < kVPrefetch; ++n) vread(tb, n);
+    // tile i+2 (complete since the barrier above) is the next Q.K's: its first K fragments
+    // are read in the last slots of this phase
+    const lds_char* nb2 = smem + ((i + 2) & (kRing - 1)) * kTileBytes;
 #pragma unroll
     for (int n = 0; n < kPvFrags; ++n) {
       __builtin_amdgcn_sched_barrier(0);
       if (n + kVPrefetch < kPvFrags) vread(tb, n + kVPrefetch);
+      if (n >= kPvFrags - kPrefetch) kread(nb2, n - (kPvFrags - kPrefetch));
       __builtin_amdgcn_sched_barrier(0);
       mfma_acc_a(o_own[n & (kHalfColBlocks - 1)], vf[n], pown[n >> 3]);
       __builtin_amdgcn_sched_barrier(0);
