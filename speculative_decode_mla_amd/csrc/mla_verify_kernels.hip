@@ -706,7 +706,8 @@ void mla_verify_partial(PartialArgs p) {
   const float inv_own = lt > 0.f ? 1.0f / lt : 0.f;
   const float inv_par = lt_par > 0.f ? 1.0f / lt_par : 0.f;
   if (row_valid && hi == 0)
-    p.lse_part[(int64_t)wi.bs * p.rows_pad + myrow] = le > 0.f ? (st.m_ref + __builtin_amdgcn_logf(le)) * kLn2 : -INFINITY;
+    // (le > 0 only if the reference is finite, and then m_ref = -nmref: one register less to keep)
+    p.lse_part[(int64_t)wi.bs * p.rows_pad + myrow] = le > 0.f ? (__builtin_amdgcn_logf(le) - nmref) * kLn2 : -INFINITY;
 
   // The wave's 64 rows x 256 columns go through the free ring as bf16 rows (stride
   // kStageRowBytes, padded against bank conflicts), then out as whole 512-B row halves.
@@ -726,7 +727,8 @@ void mla_verify_partial(PartialArgs p) {
       *(__attribute__((address_space(3))) bf16x4*)(stage + (32 + lrow) * kStageRowBytes + cb) = vp;
     }
   // stage rows 0..31 are this wave's rows, 32..63 its partner's; two rows per store instruction
-  uint16_t* part_base = p.o_part + (int64_t)wi.bs * p.rows_pad * kDv + half * (kDv / 2) + (lane & 31) * 8;
+  // (the column half from the wave index in a scalar register: keeping `half` live this long spilled it)
+  uint16_t* part_base = p.o_part + (int64_t)wi.bs * p.rows_pad * kDv + (w_uniform & 1) * (kDv / 2) + (lane & 31) * 8;
 #pragma unroll 4
   for (int k = 0; k < 32; ++k) {
     const int r = 2 * k + hi;
