@@ -710,32 +710,40 @@ void mla_verify_partial(PartialArgs p) {
     p.lse_part[(int64_t)wi.bs * p.rows_pad + myrow] = le > 0.f ? (__builtin_amdgcn_logf(le) - nmref) * kLn2 : -INFINITY;
 
   // The wave's 64 rows x 256 columns go through the free ring as bf16 rows (stride
-  // kStageRowBytes, padded against bank conflicts), then out as whole 512-B row halves.
-  // In the C layout the lane holds, per 32-column block c, columns 32c + 8*q4 + 4*hi .. +3.
+  // kStageRowBytes, padded against bank conflicts), then out as whole 512-B row halves, two rows
+  // per store instruction.  In the C layout the lane holds, per 32-column block c, columns
+  // 32c + 8*q4 + 4*hi .. +3.  The wave's own rows (stage rows 0..31) are staged first and
+  // stored while its partner's rows (stage rows 32..63) are converted, so the stores drain
+  // under the conversion work.
   typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
   lds_char* stage = smem + w * kStageBytes;
-#pragma unroll
-  for (int c = 0; c < kHalfColBlocks; ++c)
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const int cb = (32 * c + 8 * q4 + 4 * hi) * 2;
-      const bf16x4 vo = {(__bf16)(acc_read(o_own[c][4 * q4]) * inv_own), (__bf16)(acc_read(o_own[c][4 * q4 + 1]) * inv_own),
-                         (__bf16)(acc_read(o_own[c][4 * q4 + 2]) * inv_own), (__bf16)(acc_read(o_own[c][4 * q4 + 3]) * inv_own)};
-      const bf16x4 vp = {(__bf16)(acc_read(o_par[c][4 * q4]) * inv_par), (__bf16)(acc_read(o_par[c][4 * q4 + 1]) * inv_par),
-                         (__bf16)(acc_read(o_par[c][4 * q4 + 2]) * inv_par), (__bf16)(acc_read(o_par[c][4 * q4 + 3]) * inv_par)};
-      *(__attribute__((address_space(3))) bf16x4*)(stage + lrow * kStageRowBytes + cb) = vo;
-      *(__attribute__((address_space(3))) bf16x4*)(stage + (32 + lrow) * kStageRowBytes + cb) = vp;
-    }
-  // stage rows 0..31 are this wave's rows, 32..63 its partner's; two rows per store instruction
+  auto stage_block = [&](const f32x16& o, float inv, int row, int c, int q4) {
+    const int cb = (32 * c + 8 * q4 + 4 * hi) * 2;
+    const bf16x4 v = {(__bf16)(acc_read(o[4 * q4]) * inv), (__bf16)(acc_read(o[4 * q4 + 1]) * inv),
+                      (__bf16)(acc_read(o[4 * q4 + 2]) * inv), (__bf16)(acc_read(o[4 * q4 + 3]) * inv)};
+    *(__attribute__((address_space(3))) bf16x4*)(stage + row * kStageRowBytes + cb) = v;
+  };
   // (the column half from the wave index in a scalar register: keeping `half` live this long spilled it)
   uint16_t* part_base = p.o_part + (int64_t)wi.bs * p.rows_pad * kDv + (w_uniform & 1) * (kDv / 2) + (lane & 31) * 8;
-#pragma unroll 4
-  for (int k = 0; k < 32; ++k) {
+  auto store_pair = [&](int k) {  // stage rows 2k and 2k+1
     const int r = 2 * k + hi;
     const i32x4 v = *(const __attribute__((address_space(3))) i32x4*)(stage + r * kStageRowBytes + (lane & 31) * 16);
     const int grow = row0 + (r < 32 ? w * kRowsPerWave + r : partner * kRowsPerWave + r - 32);
     if (grow < R) *(i32x4*)(part_base + (int64_t)grow * kDv) = v;
-  }
+  };
+#pragma unroll
+  for (int c = 0; c < kHalfColBlocks; ++c)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) stage_block(o_own[c], inv_own, lrow, c, q4);
+#pragma unroll
+  for (int c = 0; c < kHalfColBlocks; ++c)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      stage_block(o_par[c], inv_par, 32 + lrow, c, q4);
+      if (q4 & 1) store_pair(2 * c + (q4 >> 1));  // own rows: pairs 0..15
+    }
+#pragma unroll
+  for (int k = 16; k < 32; ++k) store_pair(k);  // the partner's rows
 
   // Rows whose sums outgrew the fixed reference are redone exactly by their owner wave,
   // once both halves of the row have been written.
