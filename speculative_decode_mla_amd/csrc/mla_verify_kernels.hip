@@ -829,11 +829,12 @@ __global__ __launch_bounds__(kMergeThreads) void mla_verify_merge_kernel(MergeAr
   const float Mref = (M == -INFINITY) ? 0.f : M;
   const float Z = wave_sum(m_l > -INFINITY ? z_l * __expf(m_l - Mref) : 0.f);
   const float invZ = Z > 0.f ? 1.0f / Z : 0.f;
-  // weight of split s (wave-uniform): from the lane that loaded its LSE, or from memory past 64 splits
+  // weight of split s, exp(lse_s - M) / Z (wave-uniform): formed once by the lane that loaded its
+  // LSE, or from memory past 64 splits
+  const float w0 = lane < ns ? __expf(x0 - Mref) * invZ : 0.f;
   auto weight = [&](int s) {
-    const float x = s < 64 ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x0), s))
-                           : lse_s[(int64_t)s * p.rows_stride];
-    return s < ns ? __expf(x - Mref) * invZ : 0.f;
+    if (s < 64) return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w0), s));
+    return s < ns ? __expf(lse_s[(int64_t)s * p.rows_stride] - Mref) * invZ : 0.f;
   };
 
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
