@@ -1,4 +1,4 @@
-"""CPU oracle for MLA speculative-decoding verify attention (test infrastructure only).
+"""CPU oracles for MLA speculative-decoding verify attention and KV compaction (test infrastructure only).
 
 Only the tests, the smoke check and the benchmark's CPU-baseline leg may import
 this package.  It shares no code with the HIP path.
@@ -12,3 +12,4 @@ from .mla_verify_oracle import (  # noqa: F401
     verify_attention_split,
     visible_count,
 )
+from .kv_compact_oracle import compact_rows  # noqa: F401,E402
