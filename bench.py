@@ -94,6 +94,79 @@ def cpu_baseline(x, budget_s: float):
                       f"to the whole call ({total_q} tokens); {cores} host cores visible"}
 
 
+def _graph_us(torch, fn, reps=10, rounds=20):
+    """Median time per call of `fn`, from `rounds` replays of a graph of `reps` back-to-back calls."""
+    stream = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        fn()
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(rounds)]
+    for a, b in ev:
+        a.record(stream)
+        g.replay()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return statistics.median(a.elapsed_time(b) * 1e3 / reps for a, b in ev)
+
+
+def bench_compact(args, w, x, h, q, pool, slot_idx, seq_lens, q_lens, out, lse, nsplit):
+    """KV compaction of every row the workload references into a fresh contiguous buffer (one
+    launch, HBM-bound: each 1152-B row read once and written once), then kernel 1 and the whole
+    call over the compacted rows against the scattered ones.  Prints one JSON line."""
+    import torch
+
+    from speculative_decode_mla_amd import api
+    from speculative_decode_mla_amd import inputs as I
+
+    n = len(x.slot_idx)
+    dst = torch.empty((n, I.D_QK), dtype=torch.bfloat16, device="cuda")
+    new = torch.empty((n,), dtype=torch.int32, device="cuda")
+    api.compact(pool, slot_idx, dst, 0, new)
+    torch.cuda.synchronize()
+    # parity: the compacted rows are the generator's kv_rows bit for bit (closed form), and the
+    # verify call over them equals the scattered call bit for bit
+    exact = bool(np.array_equal(dst.view(torch.int16).cpu().numpy().view(np.uint16), x.kv_rows)
+                 and np.array_equal(new.cpu().numpy(), np.arange(n, dtype=np.int32)))
+    h.run(q, pool, slot_idx, seq_lens, q_lens, out, lse, nsplit)
+    o1, l1 = out.clone(), lse.clone()
+    h.run(q, dst, new, seq_lens, q_lens, out, lse, nsplit)
+    torch.cuda.synchronize()
+    same = bool(torch.equal(o1.view(torch.int16), out.view(torch.int16)) and torch.equal(l1, lse))
+    print(f"# compaction of {n} rows: bit-exact {exact}; verify over compacted rows bitwise equal {same}",
+          file=sys.stderr, flush=True)
+    t_c = _graph_us(torch, lambda: api.compact(pool, slot_idx, dst, 0, new))
+    moved = 2 * n * I.D_QK * 2 + 2 * n * 4  # rows read and written, slot ids read and written
+    k1_s = _graph_us(torch, lambda: h.partials(q, pool, slot_idx, seq_lens, q_lens, nsplit))
+    k1_c = _graph_us(torch, lambda: h.partials(q, dst, new, seq_lens, q_lens, nsplit))
+    run_s = _graph_us(torch, lambda: h.run(q, pool, slot_idx, seq_lens, q_lens, out, lse, nsplit))
+    run_c = _graph_us(torch, lambda: h.run(q, dst, new, seq_lens, q_lens, out, lse, nsplit))
+    gbps = moved / (t_c * 1e-6) / 1e9
+    res = {
+        "metric": "KV compaction GB/s (rows moved per launch) and kernel-1 time over compacted vs scattered rows",
+        "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1, "higher_is_better": True,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "rows": n, "row_bytes": I.D_QK * 2, "pool_slots": w.num_slots,
+                   "replay": "hipGraph, 10 launches per graph"},
+        "compact_us": round(t_c, 3),
+        "parity": {"rows_bit_exact": exact, "verify_bitwise_equal": same},
+        "partial_kernel_us": {"scattered": round(k1_s, 3), "compacted": round(k1_c, 3)},
+        "call_us": {"scattered": round(run_s, 3), "compacted": round(run_c, 3)},
+        "roofline": {"bound": "hbm", "kernel": "mla_kv_compact_kernel", "achieved": round(gbps, 1),
+                     "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 4),
+                     "traffic": None, "bytes_per_launch": moved},
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -106,6 +179,8 @@ def main():
     ap.add_argument("--eager", action="store_true", help="plain launches, no graph (for profilers)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run a plain 256 MiB device copy (reference size for HBM traffic counters)")
+    ap.add_argument("--compact", action="store_true",
+                    help="measure KV compaction of the workload's rows instead (and kernel 1 over the compacted rows)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
@@ -149,6 +224,10 @@ def main():
     h = api.MlaVerify(x.heads, w.batch, int(x.q_lens.max()), nsplit, x.num_slots, x.scale)
     step = lambda: h.run(q, pool, slot_idx, seq_lens, q_lens, out, lse, nsplit)  # noqa: E731
     part = lambda: h.partials(q, pool, slot_idx, seq_lens, q_lens, nsplit)  # noqa: E731
+    if args.compact:
+        bench_compact(args, w, x, h, q, pool, slot_idx, seq_lens, q_lens, out, lse, nsplit)
+        h.close()
+        return
 
     # parity on sampled rows (the oracle evaluates them one by one)
     step()

@@ -129,6 +129,33 @@ int mla_verify_partials(mla_verify_handle h, const void* q, const void* kv_pool,
 int mla_verify_merge(const float* o_part, const float* lse_part, const int32_t* q_lens, int32_t batch,
                      int32_t num_heads, int32_t max_q_len, int32_t nsplit, void* out, float* lse, void* stream);
 
+/*
+ * KV compaction: the "KV defragmentation" that magik.net, "The Moment of Truth"
+ * (sections "The Broader Context: From Kernel to System" and "Conclusion")
+ * names as a next step.  Copies the page_size = 1 rows of one slot list into
+ * a contiguous range of destination slots, in order:
+ *     dst_pool[dst_first + j] = kv_pool[slot_idx[j]]   for 0 <= j < n_rows,
+ * each row the whole 576-dim bf16 latent row (1152 bytes, copied bit for bit),
+ * and, when new_slot_idx is not NULL, new_slot_idx[j] = dst_first + j, so that
+ * a verify call over (dst_pool, new_slot_idx) sees the same rows in the same
+ * order as one over (kv_pool, slot_idx) and returns the same result.
+ *   kv_pool      device bf16 [*, 576], 16-byte aligned.
+ *   slot_idx     device int32 [n_rows]; each slot must be a row of kv_pool
+ *                (not checked: a slot past the pool is undefined behaviour).
+ *   n_rows       >= 0; 0 enqueues nothing.
+ *   dst_pool     device bf16 [dst_slots, 576], 16-byte aligned.  It may be
+ *                kv_pool itself as long as the destination rows are none of
+ *                the source rows.
+ *   dst_first    first destination slot; dst_first + n_rows <= dst_slots.
+ *   new_slot_idx device int32 [n_rows] or NULL; with it, dst_first + n_rows
+ *                must fit in int32.
+ *   stream       hipStream_t; one kernel launch, nothing else (capture-safe).
+ * Errors: INVALID_ARGUMENT (null pointers when n_rows > 0, negative sizes, a
+ * destination range outside [0, dst_slots), misalignment), HIP.
+ */
+int mla_verify_compact(const void* kv_pool, const int32_t* slot_idx, int64_t n_rows, void* dst_pool,
+                       int64_t dst_slots, int64_t dst_first, int32_t* new_slot_idx, void* stream);
+
 /* Free the workspace and the handle.  NULL is a no-op.  The caller must make
  * sure no enqueued call still uses the handle (synchronise its stream first). */
 int mla_verify_destroy(mla_verify_handle h);

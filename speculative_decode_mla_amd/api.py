@@ -115,6 +115,28 @@ class MlaVerify:
         return out, lse
 
 
+def compact(kv_pool, slot_idx, dst_pool, dst_first: int, new_slot_idx=None, stream=None):
+    """KV compaction: dst_pool[dst_first + j] = kv_pool[slot_idx[j]]; new_slot_idx[j] = dst_first + j.
+
+    kv_pool, dst_pool bf16 [*, 576]; slot_idx int32 [n]; new_slot_idx int32 [n] or None.
+    """
+    _need(kv_pool, "kv_pool", torch.bfloat16, 2)
+    _need(dst_pool, "dst_pool", torch.bfloat16, 2)
+    _need(slot_idx, "slot_idx", torch.int32, 1)
+    if kv_pool.shape[1] != D_QK or dst_pool.shape[1] != D_QK:
+        raise ValueError(f"pools must be [*, {D_QK}]")
+    n = slot_idx.shape[0]
+    if new_slot_idx is not None:
+        _need(new_slot_idx, "new_slot_idx", torch.int32, 1)
+        if new_slot_idx.shape[0] != n:
+            raise ValueError("new_slot_idx must have one entry per slot")
+    st = _lib.load().mla_verify_compact(_ptr(kv_pool), _ptr(slot_idx), n, _ptr(dst_pool), dst_pool.shape[0],
+                                        int(dst_first), _ptr(new_slot_idx) if new_slot_idx is not None else None,
+                                        _stream_handle(stream))
+    _lib.check("mla_verify_compact", st)
+    return dst_pool, new_slot_idx
+
+
 def merge(o_part, lse_part, q_lens, out, lse, stream=None):
     """Kernel 2 alone: reduce caller-provided split partials.
 

@@ -181,6 +181,26 @@ int mla_verify_merge(const float* o_part, const float* lse_part, const int32_t* 
   return hip_status(mlav::launch_merge(ma, static_cast<hipStream_t>(stream))) == MLA_OK ? MLA_OK : MLA_ERR_HIP;
 }
 
+int mla_verify_compact(const void* kv_pool, const int32_t* slot_idx, int64_t n_rows, void* dst_pool,
+                       int64_t dst_slots, int64_t dst_first, int32_t* new_slot_idx, void* stream) {
+  if (n_rows < 0 || dst_slots < 0 || dst_first < 0 || n_rows > INT32_MAX) return MLA_ERR_INVALID_ARGUMENT;
+  if (n_rows == 0) return MLA_OK;
+  if (kv_pool == nullptr || slot_idx == nullptr || dst_pool == nullptr) return MLA_ERR_INVALID_ARGUMENT;
+  if (dst_first > dst_slots - n_rows) return MLA_ERR_INVALID_ARGUMENT;
+  if (new_slot_idx != nullptr && dst_first + n_rows - 1 > INT32_MAX) return MLA_ERR_INVALID_ARGUMENT;
+  if (!aligned(kv_pool, 16) || !aligned(dst_pool, 16) || !aligned(slot_idx, 4) ||
+      (new_slot_idx != nullptr && !aligned(new_slot_idx, 4)))
+    return MLA_ERR_INVALID_ARGUMENT;
+  mlav::CompactArgs a;
+  a.src = static_cast<const uint16_t*>(kv_pool);
+  a.slot_idx = slot_idx;
+  a.dst = static_cast<uint16_t*>(dst_pool);
+  a.new_slot_idx = new_slot_idx;
+  a.n_rows = n_rows;
+  a.dst_first = dst_first;
+  return mlav::launch_compact(a, static_cast<hipStream_t>(stream)) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
 int mla_verify_destroy(mla_verify_handle h) {
   if (h == nullptr) return MLA_OK;
   int st = MLA_OK;

@@ -44,7 +44,18 @@ struct MergeArgs {
   int32_t part_fp32;         // 1: o_part holds fp32 values; 0: bf16
 };
 
+// KV compaction: dst[dst_first + j] = src[slot_idx[j]] (whole 1152-B rows), j < n_rows.
+constexpr int kCompactThreads = 256;
+struct CompactArgs {
+  const uint16_t* src;       // bf16 [*, 576]
+  const int32_t* slot_idx;   // [n_rows]
+  uint16_t* dst;             // bf16 [dst_first + n_rows, 576] at least
+  int32_t* new_slot_idx;     // [n_rows] or null: dst_first + j
+  int64_t n_rows, dst_first;
+};
+
 hipError_t launch_partial(const PartialArgs& a, hipStream_t stream);
+hipError_t launch_compact(const CompactArgs& a, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 
 }  // namespace mlav

@@ -25,8 +25,8 @@ def lib():
 
 
 def test_header_declares_the_boundary():
-    assert _declared() == ["mla_verify_create", "mla_verify_destroy", "mla_verify_error_string",
-                           "mla_verify_merge", "mla_verify_partials", "mla_verify_run"]
+    assert _declared() == ["mla_verify_compact", "mla_verify_create", "mla_verify_destroy",
+                           "mla_verify_error_string", "mla_verify_merge", "mla_verify_partials", "mla_verify_run"]
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -56,6 +56,16 @@ def test_host_validation_before_any_hip_call(lib):
     assert lib.mla_verify_merge(None, None, None, 1, 1, 1, 1, None, None, None) == _lib.MLA_ERR_INVALID_ARGUMENT
     assert lib.mla_verify_partials(None, None, None, None, None, None, 1, None) == _lib.MLA_ERR_INVALID_ARGUMENT
     assert lib.mla_verify_destroy(None) == _lib.MLA_OK
+    # compaction: checks come before any HIP call; an empty copy enqueues nothing
+    assert lib.mla_verify_compact(None, None, 0, None, 0, 0, None, None) == _lib.MLA_OK
+    assert lib.mla_verify_compact(None, None, 1, None, 1, 0, None, None) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert lib.mla_verify_compact(None, None, -1, None, 0, 0, None, None) == _lib.MLA_ERR_INVALID_ARGUMENT
+    fake = P(1 << 20)  # never dereferenced: every call below fails its host checks
+    assert lib.mla_verify_compact(fake, fake, 10, fake, 9, 0, None, None) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert lib.mla_verify_compact(fake, fake, 10, fake, 20, 11, None, None) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert lib.mla_verify_compact(fake, fake, 10, fake, 20, -1, None, None) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert lib.mla_verify_compact(P((1 << 20) + 8), fake, 10, fake, 20, 0, None, None) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert lib.mla_verify_compact(fake, fake, 10, fake, 1 << 40, (1 << 31) - 5, fake, None) == _lib.MLA_ERR_INVALID_ARGUMENT
     h = P()
     assert lib.mla_verify_create(None, ctypes.byref(h)) == _lib.MLA_ERR_INVALID_ARGUMENT
     bad = _lib.MlaVerifyConfig(16, 512, 512, 1, 4, 1, 4096, 0.07)
