@@ -1,4 +1,4 @@
-"""CPU oracles for MLA speculative-decoding verify attention and KV compaction (test infrastructure only).
+"""CPU oracles for MLA speculative-decoding verify attention, KV compaction and step metadata (test infrastructure only).
 
 Only the tests, the smoke check and the benchmark's CPU-baseline leg may import
 this package.  It shares no code with the HIP path.
@@ -13,3 +13,4 @@ from .mla_verify_oracle import (  # noqa: F401
     visible_count,
 )
 from .kv_compact_oracle import compact_rows  # noqa: F401,E402
+from .metadata_oracle import build_step_metadata  # noqa: F401,E402
