@@ -167,6 +167,79 @@ def bench_compact(args, w, x, h, q, pool, slot_idx, seq_lens, q_lens, out, lse, 
     print(json.dumps(res), flush=True)
 
 
+def bench_metadata(args, w, x, h, q, pool, slot_idx, seq_lens, q_lens, out, lse, nsplit):
+    """Device-side step metadata for the workload's requests, from a request-to-token table
+    (request b in table row 2b+1, rows as wide as the longest request): one launch against the
+    host path it replaces (numpy gather of the table rows + copy to the device), and inside a
+    captured step together with the verify call.  Prints one JSON line."""
+    import torch
+
+    import oracle
+    from speculative_decode_mla_amd import api
+
+    B = len(x.seq_lens)
+    width = int(x.seq_lens.max())
+    table = np.zeros((2 * B + 1, width), dtype=np.int32)
+    ids = np.array([2 * b + 1 for b in range(B)], dtype=np.int32)
+    ko = np.concatenate([[0], np.cumsum(x.seq_lens)])
+    for b in range(B):
+        table[ids[b], :x.seq_lens[b]] = x.slot_idx[ko[b]:ko[b + 1]]
+    pre = (x.seq_lens - x.q_lens).astype(np.int32)
+    dr = x.q_lens.astype(np.int32)
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
+    t_table, t_ids, t_pre, t_dr = d(table), d(ids), d(pre), d(dr)
+    cap = int(w.num_slots)
+    m_slots = torch.zeros((cap,), dtype=torch.int32, device="cuda")
+    m_seq = torch.zeros((B,), dtype=torch.int32, device="cuda")
+    m_q = torch.zeros((B,), dtype=torch.int32, device="cuda")
+    m_st = torch.zeros((1,), dtype=torch.int32, device="cuda")
+    build = lambda: api.build_metadata(t_table, t_ids, t_pre, t_dr, m_slots, m_seq, m_q, m_st)  # noqa: E731
+    build()
+    torch.cuda.synchronize()
+    hs, hseq, hql, hst = oracle.build_step_metadata(table, ids, pre, dr, cap)
+    total = len(hs)
+    exact = bool(int(m_st.item()) == hst == 0 and np.array_equal(m_slots[:total].cpu().numpy(), hs)
+                 and np.array_equal(m_seq.cpu().numpy(), hseq) and np.array_equal(m_q.cpu().numpy(), hql))
+    h.run(q, pool, slot_idx, seq_lens, q_lens, out, lse, nsplit)
+    o1 = out.clone()
+    h.run(q, pool, m_slots, m_seq, m_q, out, lse, nsplit)
+    torch.cuda.synchronize()
+    same = bool(torch.equal(o1.view(torch.int16), out.view(torch.int16)))
+    print(f"# metadata for {B} requests, {total} slots: bit-exact {exact}; verify on it bitwise equal {same}",
+          file=sys.stderr, flush=True)
+    t_dev = _graph_us(torch, build)
+    t_step = _graph_us(torch, lambda: (build(), h.run(q, pool, m_slots, m_seq, m_q, out, lse, nsplit)))
+    t_run = _graph_us(torch, lambda: h.run(q, pool, slot_idx, seq_lens, q_lens, out, lse, nsplit))
+    # the host path it replaces: gather the rows on the host, copy the three arrays to the device
+    host_slots = torch.empty((cap,), dtype=torch.int32, device="cuda")
+    ht = []
+    for _ in range(20):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        flat = np.concatenate([table[ids[b], :pre[b] + dr[b]] for b in range(B)])
+        host_slots[:len(flat)].copy_(torch.from_numpy(flat))
+        seq_lens.copy_(torch.from_numpy(pre + dr))
+        q_lens.copy_(torch.from_numpy(dr))
+        torch.cuda.synchronize()
+        ht.append((time.perf_counter() - t0) * 1e6)
+    moved = 2 * total * 4 + 4 * B * 4 + 4
+    gbps = moved / (t_dev * 1e-6) / 1e9
+    res = {
+        "metric": "device-side step metadata: us per build, beside the host gather + copy it replaces",
+        "value": round(t_dev, 3), "unit": "us/build", "n_gpus": 1, "higher_is_better": False,
+        "dtype": "int32", "data": "synthetic",
+        "config": {"workload": w.name, "requests": B, "slots": total, "table": list(table.shape),
+                   "replay": "hipGraph, 10 launches per graph"},
+        "parity": {"bit_exact": exact, "verify_bitwise_equal": same},
+        "host_gather_and_copy_us_p50": round(statistics.median(ht), 1),
+        "captured_step_us": {"metadata_and_verify": round(t_step, 3), "verify_only": round(t_run, 3)},
+        "roofline": {"bound": "hbm", "kernel": "mla_step_metadata_kernel", "achieved": round(gbps, 1),
+                     "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 5),
+                     "traffic": None, "bytes_per_launch": moved},
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -179,6 +252,8 @@ def main():
     ap.add_argument("--eager", action="store_true", help="plain launches, no graph (for profilers)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run a plain 256 MiB device copy (reference size for HBM traffic counters)")
+    ap.add_argument("--metadata", action="store_true",
+                    help="measure the device-side step-metadata build for the workload instead")
     ap.add_argument("--compact", action="store_true",
                     help="measure KV compaction of the workload's rows instead (and kernel 1 over the compacted rows)")
     args = ap.parse_args()
@@ -226,6 +301,10 @@ def main():
     part = lambda: h.partials(q, pool, slot_idx, seq_lens, q_lens, nsplit)  # noqa: E731
     if args.compact:
         bench_compact(args, w, x, h, q, pool, slot_idx, seq_lens, q_lens, out, lse, nsplit)
+        h.close()
+        return
+    if args.metadata:
+        bench_metadata(args, w, x, h, q, pool, slot_idx, seq_lens, q_lens, out, lse, nsplit)
         h.close()
         return
 

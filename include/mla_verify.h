@@ -156,6 +156,39 @@ int mla_verify_merge(const float* o_part, const float* lse_part, const int32_t* 
 int mla_verify_compact(const void* kv_pool, const int32_t* slot_idx, int64_t n_rows, void* dst_pool,
                        int64_t dst_slots, int64_t dst_first, int32_t* new_slot_idx, void* stream);
 
+/*
+ * Step metadata on the device: the verify call's index arrays built once per
+ * step from the serving side's request-to-token table, into caller-owned
+ * static buffers, so that a captured step replays with fresh metadata and no
+ * host work (magik.net, "The Moment of Truth": building combined indices once
+ * per step instead of per layer, "Interpreting the Crossover: The Marshaling
+ * Tax"; overriding the metadata replay logic with pre-allocated static
+ * buffers, "The Thinking Process"; a marshaling kernel on the GPU,
+ * "Assumptions and Their Validity").  For b < batch:
+ *     seq_lens[b] = prefix_lens[b] + draft_lens[b],   q_lens[b] = draft_lens[b],
+ *     slot_idx    = entries 0 .. seq_lens[b]-1 of table row req_ids[b], b in order
+ * (prefix_lens[b] tokens already cached, draft_lens[b] draft tokens whose rows
+ * are written at the next positions).
+ *   req_to_token device int32 [table_rows, table_stride]: row r lists the cache
+ *                slot of every position of the request in row r; only the
+ *                first table_width entries of a row may be used.
+ *   req_ids, prefix_lens, draft_lens  device int32 [batch], 0 <= batch <= 1024.
+ *   slot_idx     device int32 [slot_capacity] (slot_capacity <= INT32_MAX).
+ *   seq_lens, q_lens  device int32 [batch]; status device int32 [1].
+ *   With batch == 0 the table and the per-request pointers may be NULL (only
+ *   *status is written); with slot_capacity == 0 slot_idx may be NULL.
+ *   stream       hipStream_t; one kernel launch, no host synchronisation.
+ * Device-side checks set *status (0 = ok) to the OR of: 1 a row id outside
+ * [0, table_rows), 2 a negative length, 4 a sequence longer than table_width,
+ * 8 more than slot_capacity slots in all; then every seq_lens and q_lens entry
+ * is 0 (a verify call on them does nothing) and no slot is written.
+ * Errors (host): INVALID_ARGUMENT (null, sizes, alignment), HIP.
+ */
+int mla_verify_build_metadata(const int32_t* req_to_token, int32_t table_rows, int32_t table_width,
+                              int64_t table_stride, const int32_t* req_ids, const int32_t* prefix_lens,
+                              const int32_t* draft_lens, int32_t batch, int32_t* slot_idx, int64_t slot_capacity,
+                              int32_t* seq_lens, int32_t* q_lens, int32_t* status, void* stream);
+
 /* Free the workspace and the handle.  NULL is a no-op.  The caller must make
  * sure no enqueued call still uses the handle (synchronise its stream first). */
 int mla_verify_destroy(mla_verify_handle h);

@@ -137,6 +137,26 @@ def compact(kv_pool, slot_idx, dst_pool, dst_first: int, new_slot_idx=None, stre
     return dst_pool, new_slot_idx
 
 
+def build_metadata(req_to_token, req_ids, prefix_lens, draft_lens, slot_idx, seq_lens, q_lens, status,
+                   table_width=None, stream=None):
+    """Step metadata on the device (see mla_verify_build_metadata): all int32 device tensors;
+    req_to_token [rows, stride], slot_idx [capacity], status [1]."""
+    for t, name in ((req_ids, "req_ids"), (prefix_lens, "prefix_lens"), (draft_lens, "draft_lens"),
+                    (slot_idx, "slot_idx"), (seq_lens, "seq_lens"), (q_lens, "q_lens"), (status, "status")):
+        _need(t, name, torch.int32, 1)
+    _need(req_to_token, "req_to_token", torch.int32, 2)
+    batch = req_ids.shape[0]
+    if prefix_lens.shape[0] != batch or draft_lens.shape[0] != batch or seq_lens.shape[0] < batch \
+            or q_lens.shape[0] < batch or status.shape[0] < 1:
+        raise ValueError("inconsistent metadata shapes")
+    rows, stride = req_to_token.shape
+    st = _lib.load().mla_verify_build_metadata(
+        _ptr(req_to_token), rows, stride if table_width is None else int(table_width), stride, _ptr(req_ids),
+        _ptr(prefix_lens), _ptr(draft_lens), batch, _ptr(slot_idx), slot_idx.shape[0], _ptr(seq_lens), _ptr(q_lens),
+        _ptr(status), _stream_handle(stream))
+    _lib.check("mla_verify_build_metadata", st)
+
+
 def merge(o_part, lse_part, q_lens, out, lse, stream=None):
     """Kernel 2 alone: reduce caller-provided split partials.
 

@@ -12,7 +12,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libmla_verify.so")
-SOURCES = [os.path.join(HERE, "csrc", f) for f in ("mla_verify_api.hip", "mla_verify_kernels.hip", "mla_kv_compact.hip")]
+SOURCES = [os.path.join(HERE, "csrc", f) for f in ("mla_verify_api.hip", "mla_verify_kernels.hip", "mla_kv_compact.hip", "mla_step_metadata.hip")]
 ARCH = "gfx950"
 
 

@@ -201,6 +201,38 @@ int mla_verify_compact(const void* kv_pool, const int32_t* slot_idx, int64_t n_r
   return mlav::launch_compact(a, static_cast<hipStream_t>(stream)) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
+int mla_verify_build_metadata(const int32_t* req_to_token, int32_t table_rows, int32_t table_width,
+                              int64_t table_stride, const int32_t* req_ids, const int32_t* prefix_lens,
+                              const int32_t* draft_lens, int32_t batch, int32_t* slot_idx, int64_t slot_capacity,
+                              int32_t* seq_lens, int32_t* q_lens, int32_t* status, void* stream) {
+  // the per-request arrays are read only for b < batch, slot_idx only below slot_capacity
+  if (status == nullptr || (slot_capacity > 0 && slot_idx == nullptr) ||
+      (batch > 0 && (req_to_token == nullptr || req_ids == nullptr || prefix_lens == nullptr ||
+                     draft_lens == nullptr || seq_lens == nullptr || q_lens == nullptr)))
+    return MLA_ERR_INVALID_ARGUMENT;
+  if (table_rows < 1 || table_width < 0 || table_stride < table_width || batch < 0 ||
+      batch > mlav::kMetaMaxBatch || slot_capacity < 0 || slot_capacity > INT32_MAX)
+    return MLA_ERR_INVALID_ARGUMENT;
+  if (!aligned(req_to_token, 4) || !aligned(req_ids, 4) || !aligned(prefix_lens, 4) || !aligned(draft_lens, 4) ||
+      !aligned(slot_idx, 4) || !aligned(seq_lens, 4) || !aligned(q_lens, 4) || !aligned(status, 4))
+    return MLA_ERR_INVALID_ARGUMENT;
+  mlav::MetadataArgs a;
+  a.req_to_token = req_to_token;
+  a.req_ids = req_ids;
+  a.prefix_lens = prefix_lens;
+  a.draft_lens = draft_lens;
+  a.slot_idx = slot_idx;
+  a.seq_lens = seq_lens;
+  a.q_lens = q_lens;
+  a.status = status;
+  a.table_stride = table_stride;
+  a.slot_capacity = slot_capacity;
+  a.table_rows = table_rows;
+  a.table_width = table_width;
+  a.batch = batch;
+  return mlav::launch_step_metadata(a, static_cast<hipStream_t>(stream)) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
 int mla_verify_destroy(mla_verify_handle h) {
   if (h == nullptr) return MLA_OK;
   int st = MLA_OK;

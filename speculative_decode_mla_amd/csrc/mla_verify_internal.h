@@ -54,7 +54,24 @@ struct CompactArgs {
   int64_t n_rows, dst_first;
 };
 
+// Step metadata: lengths and packed slot list of a verify call from a request-to-token table.
+constexpr int kMetaThreads = 256;
+constexpr int kMetaMaxBatch = 1024;
+struct MetadataArgs {
+  const int32_t* req_to_token;  // [table_rows, table_stride]; row r: slots of request r by position
+  const int32_t* req_ids;       // [batch]
+  const int32_t* prefix_lens;   // [batch]
+  const int32_t* draft_lens;    // [batch]
+  int32_t* slot_idx;            // [slot_capacity]
+  int32_t* seq_lens;            // [batch]
+  int32_t* q_lens;              // [batch]
+  int32_t* status;              // [1]
+  int64_t table_stride, slot_capacity;
+  int32_t table_rows, table_width, batch;
+};
+
 hipError_t launch_partial(const PartialArgs& a, hipStream_t stream);
+hipError_t launch_step_metadata(const MetadataArgs& a, hipStream_t stream);
 hipError_t launch_compact(const CompactArgs& a, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 

@@ -25,8 +25,9 @@ def lib():
 
 
 def test_header_declares_the_boundary():
-    assert _declared() == ["mla_verify_compact", "mla_verify_create", "mla_verify_destroy",
-                           "mla_verify_error_string", "mla_verify_merge", "mla_verify_partials", "mla_verify_run"]
+    assert _declared() == ["mla_verify_build_metadata", "mla_verify_compact", "mla_verify_create",
+                           "mla_verify_destroy", "mla_verify_error_string", "mla_verify_merge",
+                           "mla_verify_partials", "mla_verify_run"]
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -66,6 +67,17 @@ def test_host_validation_before_any_hip_call(lib):
     assert lib.mla_verify_compact(fake, fake, 10, fake, 20, -1, None, None) == _lib.MLA_ERR_INVALID_ARGUMENT
     assert lib.mla_verify_compact(P((1 << 20) + 8), fake, 10, fake, 20, 0, None, None) == _lib.MLA_ERR_INVALID_ARGUMENT
     assert lib.mla_verify_compact(fake, fake, 10, fake, 1 << 40, (1 << 31) - 5, fake, None) == _lib.MLA_ERR_INVALID_ARGUMENT
+    # step metadata: host checks (never launched here)
+    bm = lib.mla_verify_build_metadata
+    assert bm(None, 1, 1, 1, fake, fake, fake, 1, fake, 1, fake, fake, fake, None) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert bm(fake, 1, 1, 1, fake, fake, fake, 1, fake, 1, fake, fake, None, None) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert bm(fake, 1, 1, 1, fake, fake, fake, 1, None, 1, fake, fake, fake, None) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert bm(fake, 0, 1, 1, fake, fake, fake, 1, fake, 1, fake, fake, fake, None) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert bm(fake, 1, 8, 4, fake, fake, fake, 1, fake, 1, fake, fake, fake, None) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert bm(fake, 1, 1, 1, fake, fake, fake, 1025, fake, 1, fake, fake, fake, None) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert bm(fake, 1, 1, 1, fake, fake, fake, 1, fake, 1 << 31, fake, fake, fake, None) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert bm(fake, 1, 1, 1, fake, fake, fake, 1, P((1 << 20) + 2), 1, fake, fake, fake, None) == \
+        _lib.MLA_ERR_INVALID_ARGUMENT
     h = P()
     assert lib.mla_verify_create(None, ctypes.byref(h)) == _lib.MLA_ERR_INVALID_ARGUMENT
     bad = _lib.MlaVerifyConfig(16, 512, 512, 1, 4, 1, 4096, 0.07)
