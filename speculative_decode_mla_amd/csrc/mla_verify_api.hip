@@ -13,6 +13,7 @@ struct mla_verify_s {
   int device;
   int32_t row_groups;
   int32_t rows_pad;
+  int32_t streams;    // kernel 1 form: 1 (128-row workgroups) or 2 (64-row workgroups, two key streams)
   uint16_t* o_part;  // bf16 [B, max_nsplit, rows_pad, 512]
   float* lse_part;  // [B, max_nsplit, rows_pad]
 };
@@ -54,8 +55,12 @@ int mla_verify_create(const mla_verify_config* cfg, mla_verify_handle* out) {
   if (!(cfg->sm_scale > 0.f) || !std::isfinite(cfg->sm_scale)) return MLA_ERR_INVALID_ARGUMENT;
   if (cfg->d_qk != MLA_VERIFY_D_QK || cfg->d_v != MLA_VERIFY_D_V) return MLA_ERR_UNSUPPORTED;
   const int64_t rows = (int64_t)cfg->max_q_len * cfg->num_heads;
-  const int64_t row_groups = (rows + mlav::kRowsPerGroup - 1) / mlav::kRowsPerGroup;
-  const int64_t rows_pad = row_groups * mlav::kRowsPerGroup;
+  // Requests of at most 64 rows (a q_len = 1 decode step with H <= 64) use the two-stream form of
+  // kernel 1, whose workgroups hold 64 rows; larger ones the 128-row form.
+  const int32_t streams = rows <= mlav::kRowsPerGroup2s ? 2 : 1;
+  const int64_t group = streams == 2 ? mlav::kRowsPerGroup2s : mlav::kRowsPerGroup;
+  const int64_t row_groups = (rows + group - 1) / group;
+  const int64_t rows_pad = row_groups * group;
   const int64_t grid = (int64_t)cfg->batch * cfg->max_nsplit * row_groups;
   if (rows_pad > INT32_MAX / 2 || grid > INT32_MAX || (int64_t)cfg->batch * rows > INT32_MAX)
     return MLA_ERR_INVALID_ARGUMENT;
@@ -69,6 +74,7 @@ int mla_verify_create(const mla_verify_config* cfg, mla_verify_handle* out) {
   h->device = dev;
   h->row_groups = (int32_t)row_groups;
   h->rows_pad = (int32_t)rows_pad;
+  h->streams = streams;
   int st = hip_status(hipMalloc((void**)&h->o_part, (size_t)partial_rows * mlav::kDv * sizeof(uint16_t)));
   if (st == MLA_OK) st = hip_status(hipMalloc((void**)&h->lse_part, (size_t)partial_rows * sizeof(float)));
   if (st != MLA_OK) {
@@ -112,6 +118,7 @@ int launch_partials(mla_verify_handle h, const void* q, const void* kv_pool, con
   pa.row_groups = h->row_groups;
   pa.rows_pad = h->rows_pad;
   pa.min_tiles = kMinTilesPerSplit;
+  pa.streams = h->streams;
   pa.scale_log2 = c.sm_scale * 1.4426950408889634f;
   return mlav::launch_partial(pa, s) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }

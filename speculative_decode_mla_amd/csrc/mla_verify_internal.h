@@ -14,6 +14,7 @@ constexpr int kWaves = 4;            // waves per workgroup (one per SIMD)
 constexpr int kRowsPerWave = 32;     // (token, head) rows owned by one wave
 constexpr int kRowsPerGroup = kWaves * kRowsPerWave;  // rows per workgroup: 128
 constexpr int kTileKeys = 32;        // keys gathered into LDS per step (one MFMA block)
+constexpr int kRowsPerGroup2s = 2 * kRowsPerWave;  // rows per workgroup in the two-stream form: 64
 
 // Kernel 1: one workgroup per (request, split, 128-row group).
 struct PartialArgs {
@@ -27,7 +28,8 @@ struct PartialArgs {
   int32_t batch, heads, max_q_len, nsplit;
   int32_t row_groups;        // ceil(max_q_len*H / 128)
   int32_t rows_pad;          // row_groups * 128
-  int32_t min_tiles;         // fewest 64-key tiles a split is given (caps the split count)
+  int32_t min_tiles;         // fewest 32-key tiles a split is given (caps the split count)
+  int32_t streams;           // 1: 128-row workgroups; 2: 64-row workgroups over two key streams
   float scale_log2;          // sm_scale * log2(e)
 };
 

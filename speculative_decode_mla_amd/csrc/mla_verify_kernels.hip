@@ -256,7 +256,7 @@ struct WorkItem {
 // Decode a workgroup id; false if the workgroup has nothing to do.  The row
 // groups that read the same keys get ids that are equal mod 8: workgroups are
 // dispatched round-robin over the 8 XCDs, so those groups share one XCD's L2.
-__device__ __forceinline__ bool decode_work(const PartialArgs& p, int wg, WorkItem& wi) {
+__device__ __forceinline__ bool decode_work(const PartialArgs& p, int wg, int rows_per_group, WorkItem& wi) {
   const int nbs = p.batch * p.nsplit;
   if ((nbs & 7) == 0) {
     const int x = wg & 7, k = wg >> 3;
@@ -271,7 +271,7 @@ __device__ __forceinline__ bool decode_work(const PartialArgs& p, int wg, WorkIt
   wi.L = p.seq_lens[wi.b];
   wi.Q = clamped_q(p.q_lens, p.seq_lens, wi.b, p.max_q_len);
   wi.R = wi.Q * p.heads;
-  if (wi.Q <= 0 || wi.g * kRowsPerGroup >= wi.R) return false;
+  if (wi.Q <= 0 || wi.g * rows_per_group >= wi.R) return false;
   const int ns = split_count(wi.L, p.nsplit, p.min_tiles);
   if (wi.s >= ns) return false;
   const int tiles = (wi.L + kTileKeys - 1) / kTileKeys;
@@ -292,9 +292,11 @@ __device__ __forceinline__ bool decode_work(const PartialArgs& p, int wg, WorkIt
 // a time across the whole wave, with a running max and a rescale at every key,
 // in fp32.  Overwrites the row's partial.  Only reached for such rows, so its
 // speed does not matter.
-__device__ __forceinline__ void redo_rows_exact(const PartialArgs& p, const WorkItem& wi, int row_base, uint32_t rows) {
+// The partial's keys are the split's tiles tile_first, tile_first + tile_step, ...; it is stored as
+// partial `part` (rows_pad rows each).
+__device__ __forceinline__ void redo_rows_exact(const PartialArgs& p, const WorkItem& wi, int row_base, uint32_t rows,
+                                                int tile_first, int tile_step, int64_t part) {
   const int lane = threadIdx.x & 63;
-  const int key_begin = wi.t_begin * kTileKeys;
   const int key_end = min(wi.L, wi.t_end * kTileKeys);
   const int32_t* slots = p.slot_idx + wi.ko;
   while (rows != 0) {
@@ -309,7 +311,8 @@ __device__ __forceinline__ void redo_rows_exact(const PartialArgs& p, const Work
     for (int d = 0; d < 9; ++d) qv[d] = bf16f(qrow[d * 64 + lane]);
     float m = -INFINITY, l = 0.f;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int key = key_begin; key < kend; ++key) {
+    for (int key = (wi.t_begin + tile_first) * kTileKeys; key < kend;
+         key += (key + 1) % kTileKeys == 0 ? 1 + (tile_step - 1) * kTileKeys : 1) {  // skip the other stream's tiles
       const uint16_t* krow = p.kv + (int64_t)slots[key] * kDqk;
       float dot = 0.f;
 #pragma unroll
@@ -324,7 +327,7 @@ __device__ __forceinline__ void redo_rows_exact(const PartialArgs& p, const Work
       m = m_new;
     }
     const float inv = l > 0.f ? 1.0f / l : 0.f;
-    const int64_t prow = (int64_t)wi.bs * p.rows_pad + row;
+    const int64_t prow = part * p.rows_pad + row;
     bf16x8 ov;
 #pragma unroll
     for (int j = 0; j < 8; ++j) ov[j] = (__bf16)(acc[j] * inv);
@@ -414,7 +417,7 @@ void mla_verify_partial(PartialArgs p) {
   lds_char* xchg = smem + kRing * kTileBytes;  // [2][kWaves][2 KiB]: bf16 P of each wave, double-buffered
 
   WorkItem wi;
-  if (!decode_work(p, blockIdx.x, wi)) return;
+  if (!decode_work(p, blockIdx.x, kRowsPerGroup, wi)) return;
   const int L = wi.L, Q = wi.Q, H = p.heads, R = wi.R;
   const int ntiles = wi.t_end - wi.t_begin;
 
@@ -749,7 +752,7 @@ void mla_verify_partial(PartialArgs p) {
   // once both halves of the row have been written.
   if (any_redo) {
     __syncthreads();  // (global writes of both halves are ordered by the barrier's release/acquire)
-    if (redo != 0) redo_rows_exact(p, wi, row0 + w * kRowsPerWave, (uint32_t)redo);
+    if (redo != 0) redo_rows_exact(p, wi, row0 + w * kRowsPerWave, (uint32_t)redo, 0, 1, wi.bs);
   }
 }
 
@@ -765,6 +768,318 @@ constexpr int kMergeUnroll = 8;
 
 // Eight consecutive partial values: loaded raw (so that a batch of loads is in flight at
 // once), widened to fp32 when used.
+// Kernel 1, two-stream form, for requests of at most 64 (token, head) rows (a q_len = 1 decode
+// step with H <= 64, or a few draft tokens with few heads).  A 128-row workgroup would spend half
+// of its MFMA work on rows that do not exist; here the four waves form two streams of a wave pair,
+// both over the same 64 rows (wave 2s + h: stream s, rows [32h, 32h + 32), output columns
+// [256h, 256h + 256)).  Stream s takes tiles s, s + 2, s + 4, ... of the split, so one step consumes
+// two tiles.  Each stream's tiles are double-buffered in two of the four ring buffers: the next
+// tile is gathered between the Q.K MFMAs of the current one, into the buffer every wave finished
+// with at the step's first barrier.  (The one-tile-ahead Q.K of the 128-row form would need three
+// buffers per stream, which do not fit, so here the softmax sits between the two contractions of a
+// tile.)  At the end the two streams are merged inside the workgroup and one partial per split is
+// written, as in the 128-row form.
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+void mla_verify_partial_2s(PartialArgs p) {
+  __shared__ __attribute__((aligned(1024))) char smem_raw[kRing * kTileBytes + kXchgBytes];
+  lds_char* smem = (lds_char*)smem_raw;
+  lds_char* xchg = smem + kRing * kTileBytes;  // [2][kWaves][2 KiB]: bf16 P of each wave, double-buffered
+
+  WorkItem wi;
+  if (!decode_work(p, blockIdx.x, kRowsPerGroup2s, wi)) return;
+  const int L = wi.L, Q = wi.Q, H = p.heads, R = wi.R;
+  const int ntiles = wi.t_end - wi.t_begin;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int hi = lane >> 5, lrow = lane & 31;
+  const int stream = w >> 1;
+  const int half = w & 1;
+  const int partner = w ^ 1;
+  const int row0 = wi.g * kRowsPerGroup2s;
+  const int myrow = row0 + half * kRowsPerWave + lrow;
+  const bool row_valid = myrow < R;
+  const int tok = row_valid ? myrow / H : 0;
+  const int limit = L - Q + tok + 1;  // this row sees keys [0, limit)
+  const int mask_from = L - Q + 1;    // first key some draft row cannot see
+  const int nst = (ntiles - stream + 1) / 2;  // this stream's tiles
+  const int nsteps = (ntiles + 1) / 2;        // stream 0 has the most
+
+  // ---- gather set-up: wave (s, h) moves key blocks 2h and 2h + 1 (keys 16h .. 16h + 15) of its
+  // stream's tiles; keys past the request's end use its last key's row (scores masked) ----------
+  const int g_kr = lane >> 3;
+  const char* kv = (const char*)p.kv;
+  const uint32_t smem_base = (uint32_t)(uintptr_t)smem;
+  const int w_uniform = __builtin_amdgcn_readfirstlane(w);
+  const int32_t* slots_g = p.slot_idx + wi.ko;
+  auto buf_of = [&](int k) { return (w_uniform >> 1) + 2 * (k & 1); };  // ring buffer of the stream's tile k
+  auto gather_key = [&](int k, int j) {
+    const int kk = k < nst ? k : (nst > 0 ? nst - 1 : 0);
+    const int key = (wi.t_begin + 2 * kk + stream) * kTileKeys + 16 * half + 8 * j + g_kr;
+    return key < L ? key : L - 1;
+  };
+  auto g_row = [&](int slot, int j) { return kv + (int64_t)slot * kRowBytes + (((lane & 7) ^ g_kr ^ j) << 4); };
+  auto g_lds = [&](int k, int j) {
+    return smem_base + buf_of(k) * kTileBytes + (2 * (w_uniform & 1) + j) * kKeyBlockBytes;
+  };
+
+  // Q.K A operand: lane reads key lrow, 16-B chunk 2*ks + hi (relative to a tile buffer)
+  int kaddr[4];
+  {
+    const int kr = lrow & 7, f = kr ^ ((lrow >> 3) & 1);
+    const int base = (lrow >> 3) * kKeyBlockBytes + kr * 128;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) kaddr[j] = base + (((2 * j) ^ hi ^ f) << 4);
+  }
+
+  // ---- prologue: slot indices of tile 0, the q rows staged through ring buffer w (as in the
+  // 128-row form), then tile 0 ----------------------------------------------------------------
+  int sl[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) sl[j] = load_b32_untracked(slots_g + gather_key(0, j));
+  {
+    const uint32_t qbuf = smem_base + w_uniform * kTileBytes;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const int r = row0 + half * kRowsPerWave + 8 * kb + g_kr;
+      const int64_t qrow = wi.qo * H + (r < R ? r : 0);
+      dma_key_block((const char*)(p.q + qrow * kDqk) + (((lane & 7) ^ g_kr ^ (kb & 1)) << 4), qbuf + kb * kKeyBlockBytes);
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" : "+v"(sl[0]), "+v"(sl[1]) : : "memory");
+  bf16x8 qf[kQkSteps];
+  {
+    const lds_char* qb = smem + w * kTileBytes;
+#pragma unroll
+    for (int ks = 0; ks < kQkSteps; ++ks)
+      qf[ks] = *(const __attribute__((address_space(3))) bf16x8*)(qb + kaddr[ks & 3] + (ks >> 2) * kBlockBytes);
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
+  __syncthreads();
+  if (nst > 0) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) dma_key_block(g_row(sl[j], j), g_lds(0, j));
+  }
+  int sn[2];  // slots of the next tile to gather (compiler-tracked loads, awaited at the next step)
+#pragma unroll
+  for (int j = 0; j < 2; ++j) sn[j] = slots_g[gather_key(1, j)];
+
+  // P.V A operand addresses, as in the 128-row form (this wave's column half folded in)
+  int vaddr[2][2];
+  {
+    const int G = lane >> 4, j = lane & 15;
+    const int kr = 4 * (G >> 1) + (j >> 2);
+    const int u = 2 * (G & 1) + ((j & 3) >> 1);
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+        vaddr[e][r] = half * 4 * kBlockBytes + r * kKeyBlockBytes + kr * 128 + (((4 * e) ^ u ^ kr ^ r) << 4) +
+                      (j & 1) * 8;
+  }
+  f32x16 o_own[kHalfColBlocks], o_par[kHalfColBlocks];
+#pragma unroll
+  for (int c = 0; c < kHalfColBlocks; ++c) {
+    o_own[c] = (f32x16){};
+    o_par[c] = (f32x16){};
+    // zeroed here, in AGPRs: left alone, the compiler moved the zeroing down to just before the
+    // first P.V MFMA inside the loop, with no wait states between the write and the MFMA
+    asm volatile("" : "+a"(o_own[c]), "+a"(o_par[c]));
+  }
+  RowSoftmax st{-INFINITY, 0.f, 0.f};
+  float nmref = 0.f;
+  bf16x8 kf[kQkSteps];
+  auto kread = [&](const lds_char* tb, int ks) {
+    kf[ks] = *(const __attribute__((address_space(3))) bf16x8*)(tb + kaddr[ks & 3] + (ks >> 2) * kBlockBytes);
+  };
+  bf16x8 vf[kPvFrags];
+  auto vread = [&](const lds_char* tb, int n) {
+    const int cbl = n & (kHalfColBlocks - 1), kk = n >> 3;
+    const lds_char* vb = tb + (cbl >> 1) * kBlockBytes + kk * 2 * kKeyBlockBytes;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)(vb + vaddr[cbl & 1][0]));
+    const i16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)(vb + vaddr[cbl & 1][1]));
+    vf[n] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+
+  for (int k = 0; k < nsteps; ++k) {
+    const bool active = k < nst;
+    const lds_char* tb = smem + buf_of(k) * kTileBytes;
+    MLAV_WAIT_VMCNT(0);  // this stream's tile k (and the slot loads for the next gather) have landed
+    __syncthreads();     // every stream's tile k is visible; every wave is done with step k-1
+    const bool refill = k + 1 < nst;
+    const char* r0 = g_row(sn[0], 0);
+    const char* r1 = g_row(sn[1], 1);
+    if (refill) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) sn[j] = slots_g[gather_key(k + 2, j)];
+    }
+    const uint32_t l0 = g_lds(k + 1, 0), l1 = g_lds(k + 1, 1);
+    SoftmaxTile sm;
+    lds_char* xw = xchg + (k & 1) * (kWaves * 2048) + w * 2048 + lane * 16;
+    if (active) {
+      // Q.K of tile k, the gathers of the stream's tile k+1 between its MFMAs
+      f32x16 sacc;
+#pragma unroll
+      for (int ks = 0; ks < kPrefetch; ++ks) kread(tb, ks);
+#pragma unroll
+      for (int ks = 0; ks < kQkSteps; ++ks) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (ks + kPrefetch < kQkSteps) kread(tb, ks + kPrefetch);
+        __builtin_amdgcn_sched_barrier(0);
+        if (ks == 0) mfma_first_v(sacc, kf[ks], qf[ks]);
+        else mfma_acc_v(sacc, kf[ks], qf[ks]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (refill && !(ks & 1) && (ks >> 1) < 2 * kDmaPerTile) {
+          const int j = ks >> 1;
+          if (j < kDmaPerTile) dma_chunk_group(r0, l0, j);
+          else dma_chunk_group(r1, l1, j - kDmaPerTile);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile(MLAV_MFMA_DRAIN : "+v"(sacc));
+      const int t = wi.t_begin + 2 * k + stream;
+      if (t * kTileKeys + kTileKeys > mask_from) mask_tile(sacc, t * kTileKeys + 4 * hi, limit);
+      if (k == 0) {  // the stream's reference: the row max of its first tile (see the 128-row form)
+        st.m_ref = tile_row_max(sacc) * p.scale_log2;
+        nmref = (st.m_ref == -INFINITY) ? 0.f : -st.m_ref;
+      }
+      scale_scores(sm, sacc, nmref, p.scale_log2);
+#pragma unroll
+      for (int slot = 0; slot < kSoftmaxSlots; ++slot) softmax_slot(slot, sm);
+      *(__attribute__((address_space(3))) i32x4*)(xw) = sm.operand(0);
+      *(__attribute__((address_space(3))) i32x4*)(xw + 1024) = sm.operand(1);
+    }
+    __syncthreads();  // the partner's P is visible
+    if (active) {
+      const bf16x8 pown[2] = {__builtin_bit_cast(bf16x8, sm.operand(0)), __builtin_bit_cast(bf16x8, sm.operand(1))};
+      bf16x8 ppar[2];
+      {
+        const lds_char* xp = xchg + (k & 1) * (kWaves * 2048) + partner * 2048 + lane * 16;
+        ppar[0] = *(const __attribute__((address_space(3))) bf16x8*)(xp);
+        ppar[1] = *(const __attribute__((address_space(3))) bf16x8*)(xp + 1024);
+      }
+#pragma unroll
+      for (int n = 0; n < kVPrefetch; ++n) vread(tb, n);
+#pragma unroll
+      for (int n = 0; n < kPvFrags; ++n) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (n + kVPrefetch < kPvFrags) vread(tb, n + kVPrefetch);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_acc_a(o_own[n & (kHalfColBlocks - 1)], vf[n], pown[n >> 3]);
+        __builtin_amdgcn_sched_barrier(0);
+        sum_slot(n, sm, st);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_acc_a(o_par[n & (kHalfColBlocks - 1)], vf[n], ppar[n >> 3]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  MLAV_WAIT_VMCNT(0);  // the last slot loads
+  // The accumulators are read below only through acc_read (volatile), which stays behind this drain.
+  asm volatile(MLAV_MFMA_DRAIN);
+
+  // ---- merge of the two streams, then the partial write (one partial per split, as in the
+  // 128-row form).  Each stream's sums and accumulators are relative to its own reference m_s;
+  // with m = max(m_0, m_1) and a_s = 2^(m_s - m), the split's are l = sum_s a_s l_s and
+  // O = sum_s a_s O_s.  Stream 1 hands over its per-row (m, l, l_exact) and, in two column halves
+  // (to fit beside the staging rows), its accumulators through LDS; stream 0 combines, normalises
+  // and stores.  A row where either stream's sum outgrew its reference is redone exactly over
+  // the whole split.
+  const float lt = pair_sum(st.l_run);
+  const float le = pair_sum(st.l_exact);
+  __syncthreads();  // every wave is done with the ring and the P exchange buffers
+  float* stat = (float*)(smem_raw + kRing * kTileBytes);  // [wave][32 rows][3]: m_ref, l, l_exact
+  if (hi == 0) {
+    stat[(w * 32 + lrow) * 3 + 0] = st.m_ref;
+    stat[(w * 32 + lrow) * 3 + 1] = lt;
+    stat[(w * 32 + lrow) * 3 + 2] = le;
+  }
+  __syncthreads();
+  // this lane's own row (32*half + lrow) and partner row (32*(1-half) + lrow): stream 0 holds them
+  // in waves half and 1-half, stream 1 in waves 2+half and 3-half
+  struct Comb { float a0, a1, inv, lex, m; bool redo; };
+  auto combine = [&](int wa) {
+    const float* s0 = stat + (wa * 32 + lrow) * 3;
+    const float* s1 = stat + ((wa + 2) * 32 + lrow) * 3;
+    Comb c;
+    c.m = fmaxf(s0[0], s1[0]);
+    c.a0 = s0[0] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s0[0] - c.m);
+    c.a1 = s1[0] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s1[0] - c.m);
+    const float l = s0[1] * c.a0 + s1[1] * c.a1;
+    c.lex = s0[2] * c.a0 + s1[2] * c.a1;
+    c.inv = l > 0.f ? 1.0f / l : 0.f;
+    c.redo = !(s0[2] < kRowSumLimit) || !(s1[2] < kRowSumLimit);  // incl. +inf / NaN
+    return c;
+  };
+  const Comb co = combine(half), cp = combine(1 - half);
+  const bool any_redo = __ballot(co.redo || cp.redo) != 0;  // the wave's lanes cover all 64 rows
+  const uint64_t redo = __ballot(co.redo && hi == 0 && row_valid);
+  if (stream == 0 && row_valid && hi == 0)
+    p.lse_part[(int64_t)wi.bs * p.rows_pad + myrow] =
+        co.lex > 0.f ? (co.m + __builtin_amdgcn_logf(co.lex)) * kLn2 : -INFINITY;
+
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  lds_char* stage = smem + (w & 1) * kStageBytes;               // stream 0's staging rows
+  lds_char* dump = smem + 2 * kStageBytes + (w & 1) * 32 * 1024;  // stream 1's accumulators, one half
+  static_assert(2 * kStageBytes + 2 * 32 * 1024 <= kRing * kTileBytes, "staging and hand-over fit the ring");
+#pragma unroll
+  for (int ph = 0; ph < 2; ++ph) {
+    if (stream == 1) {  // column blocks 4ph .. 4ph+3: own and partner rows, 4 values per (c, q4)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x16& oo = o_own[4 * ph + c];
+          const f32x16& op = o_par[4 * ph + c];
+          const f32x4 vo = {acc_read(oo[4 * q4]), acc_read(oo[4 * q4 + 1]), acc_read(oo[4 * q4 + 2]), acc_read(oo[4 * q4 + 3])};
+          const f32x4 vp = {acc_read(op[4 * q4]), acc_read(op[4 * q4 + 1]), acc_read(op[4 * q4 + 2]), acc_read(op[4 * q4 + 3])};
+          const int j = (c * 4 + q4) * 2;
+          *(__attribute__((address_space(3))) f32x4*)(dump + (j * 64 + lane) * 16) = vo;
+          *(__attribute__((address_space(3))) f32x4*)(dump + ((j + 1) * 64 + lane) * 16) = vp;
+        }
+    }
+    __syncthreads();  // the half of stream 1's accumulators is in LDS
+    if (stream == 0) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x16& oo = o_own[4 * ph + c];
+          const f32x16& op = o_par[4 * ph + c];
+          const int j = (c * 4 + q4) * 2;
+          const f32x4 do_ = *(const __attribute__((address_space(3))) f32x4*)(dump + (j * 64 + lane) * 16);
+          const f32x4 dp = *(const __attribute__((address_space(3))) f32x4*)(dump + ((j + 1) * 64 + lane) * 16);
+          const int cb = (32 * (4 * ph + c) + 8 * q4 + 4 * hi) * 2;
+          bf16x4 vo, vp;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            vo[e] = (__bf16)((acc_read(oo[4 * q4 + e]) * co.a0 + do_[e] * co.a1) * co.inv);
+            vp[e] = (__bf16)((acc_read(op[4 * q4 + e]) * cp.a0 + dp[e] * cp.a1) * cp.inv);
+          }
+          *(__attribute__((address_space(3))) bf16x4*)(stage + lrow * kStageRowBytes + cb) = vo;
+          *(__attribute__((address_space(3))) bf16x4*)(stage + (32 + lrow) * kStageRowBytes + cb) = vp;
+        }
+    }
+    if (ph == 0) __syncthreads();  // stream 0 has read the first half before stream 1 writes the second
+  }
+  if (stream == 0) {
+    // stage rows 0..31 are this wave's rows, 32..63 its partner's; two rows per store instruction
+    uint16_t* part_base = p.o_part + (int64_t)wi.bs * p.rows_pad * kDv + (w_uniform & 1) * (kDv / 2) + (lane & 31) * 8;
+#pragma unroll 4
+    for (int k = 0; k < 32; ++k) {
+      const int r = 2 * k + hi;
+      const i32x4 v = *(const __attribute__((address_space(3))) i32x4*)(stage + r * kStageRowBytes + (lane & 31) * 16);
+      const int grow = row0 + (r < 32 ? half * kRowsPerWave + r : (1 - half) * kRowsPerWave + r - 32);
+      if (grow < R) *(i32x4*)(part_base + (int64_t)grow * kDv) = v;
+    }
+  }
+  if (any_redo) {
+    __syncthreads();  // (global writes of both halves are ordered by the barrier's release/acquire)
+    if (stream == 0 && redo != 0) redo_rows_exact(p, wi, row0 + half * kRowsPerWave, (uint32_t)redo, 0, 1, wi.bs);
+  }
+}
+
 template <typename PartT>
 struct Raw8;
 template <>
@@ -869,7 +1184,10 @@ __global__ __launch_bounds__(kMergeThreads) void mla_verify_merge_kernel(MergeAr
 
 hipError_t launch_partial(const PartialArgs& a, hipStream_t stream) {
   const int64_t grid = (int64_t)a.batch * a.nsplit * a.row_groups;
-  hipLaunchKernelGGL(mla_verify_partial, dim3((unsigned)grid), dim3(kWaves * 64), 0, stream, a);
+  if (a.streams == 2)
+    hipLaunchKernelGGL(mla_verify_partial_2s, dim3((unsigned)grid), dim3(kWaves * 64), 0, stream, a);
+  else
+    hipLaunchKernelGGL(mla_verify_partial, dim3((unsigned)grid), dim3(kWaves * 64), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -1,0 +1,101 @@
+"""GPU parity for q_len = 1 decode steps (and other requests of at most 64 rows), which run the
+two-stream form of kernel 1: against the fp64 oracle, max |out err| <= 1e-2, max |lse err| <= 1e-3.
+All calls go through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from speculative_decode_mla_amd import inputs as I
+from tests.gpu_helpers import LSE_TOL, OUT_TOL, DeviceInputs, bf16_to_f64, max_errors
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def api():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from speculative_decode_mla_amd import api as A
+    return A
+
+
+def _run_check(api, x, nsplit, label, max_q=None):
+    d = DeviceInputs(x)
+    h = api.MlaVerify(x.heads, len(x.seq_lens), max_q or int(max(1, x.q_lens.max())), nsplit, x.num_slots, x.scale)
+    out, lse = d.run(h, nsplit)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle.verify_attention(x.q, x.pool(), x.slot_idx, x.seq_lens, x.q_lens, x.scale)
+    eo, el = max_errors(out, lse, ref_o, ref_l)
+    print(f"{label} nsplit={nsplit}: max|out err|={eo:.3e} max|lse err|={el:.3e}", flush=True)
+    assert eo <= OUT_TOL and el <= LSE_TOL
+    return out, lse
+
+
+CASES = [
+    # (seed, seq_lens, q_lens, heads, nsplit)
+    (50, [1000], [1], 64, 4),
+    (51, [33], [1], 64, 1),            # two tiles: each stream one
+    (52, [31], [1], 64, 1),            # one tile: the second stream has none (empty partial)
+    (53, [290], [1], 64, 2),           # ten tiles
+    (54, [257, 1, 4000, 64], [1, 1, 1, 1], 64, 8),  # ragged batch, a one-key request
+    (55, [700, 1500], [2, 1], 32, 4),  # 64 rows from two draft tokens x 32 heads
+    (56, [999], [1], 48, 3),           # 48 rows: a part-filled group
+    (57, [8 * 32 * 3 + 5], [1], 64, 3),  # 25 tiles over three splits: odd tile counts per split
+]
+
+
+@pytest.mark.parametrize("seed,lens,qlens,heads,nsplit", CASES)
+def test_decode_cases(api, seed, lens, qlens, heads, nsplit):
+    x = I.make_custom(np.random.default_rng(seed), lens, qlens, heads, int(sum(lens)) * 2 + 64)
+    _run_check(api, x, nsplit, f"decode case {seed}")
+
+
+def test_decode_split_count_does_not_change_result(api):
+    x = I.make_custom(np.random.default_rng(58), [5000], [1], 64, 12000)
+    outs = []
+    for ns in (1, 3, 16, 64):
+        out, _ = _run_check(api, x, ns, "decode split-count", max_q=1)
+        outs.append(bf16_to_f64(out))
+    assert max(np.max(np.abs(o - outs[0])) for o in outs) <= OUT_TOL
+
+
+def test_decode_overflow_fallback_rows(api):
+    """A key far above its stream's first-tile max (in the second stream's tiles) sends the row
+    through the exact fallback over the whole split (the two streams are merged before the write)."""
+    x = I.make_custom(np.random.default_rng(59), [3000], [1], 64, 6000)
+    # key 2920 sits in tile 91: local tile 91 of the one split (nsplit 1) and 29 of the third split
+    # (nsplit 3 -> splits start at tiles 0, 31, 62), odd in both, so the second stream takes it.
+    # It is head 7's query with the span of the other 63 heads' queries projected out, times 2.5:
+    # ~92 nats for head 7 (2^(x - m_ref) overflows fp32), ~0 for every other head, and its v
+    # (dims 0..511) stays ~2.5 N(0,1), so head 7's exact redo is the only row it moves.
+    qh = oracle.bf16_bits_to_f64(x.q[0])
+    others = np.delete(qh, 7, axis=0)
+    coef, *_ = np.linalg.lstsq(others.T, qh[7], rcond=None)
+    perp = qh[7] - others.T @ coef
+    x.kv_rows[2920] = I.f32_to_bf16_bits((2.5 * perp).astype(np.float32))
+    _run_check(api, x, 3, "decode overflow-inf")
+    _run_check(api, x, 1, "decode overflow-inf")
+
+
+@pytest.mark.parametrize("workload", ["decode64k", "decode_batch16"])
+def test_decode_full_size_sampled_parity(api, workload):
+    w = I.WORKLOADS[workload]
+    x = I.make_inputs(workload)
+    d = DeviceInputs(x)
+    h = api.MlaVerify(x.heads, w.batch, 1, w.nsplit, x.num_slots, x.scale)
+    out, lse = d.run(h, w.nsplit)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(98)
+    rows = [(b, 0) for b in range(w.batch)] + [(b, x.heads - 1) for b in range(w.batch)]
+    rows += [(int(t), int(hh)) for t, hh in zip(rng.integers(0, w.batch, 16), rng.integers(0, x.heads, 16))]
+    ro, rl = oracle.verify_attention_rows(x.q, x.sparse_pool(), x.slot_idx, x.seq_lens, x.q_lens, x.scale, rows)
+    o = out.float().cpu().numpy()
+    l = lse.cpu().numpy()
+    eo = max(float(np.max(np.abs(o[t, hh] - ro[i]))) for i, (t, hh) in enumerate(rows))
+    el = max(abs(float(l[t, hh]) - rl[i]) for i, (t, hh) in enumerate(rows))
+    print(f"{workload} nsplit={w.nsplit}, {len(rows)} sampled rows: max|out err|={eo:.3e} max|lse err|={el:.3e}",
+          flush=True)
+    assert eo <= OUT_TOL and el <= LSE_TOL
+    del d, h
+    torch.cuda.empty_cache()

@@ -10,7 +10,7 @@ from speculative_decode_mla_amd import build
 from tests import asm_hazards
 
 KERNELS = os.path.join(build.HERE, "csrc", "mla_verify_kernels.hip")
-FUNCTIONS = ["_ZN4mlav18mla_verify_partialENS_11PartialArgsE"]
+FUNCTIONS = ["_ZN4mlav18mla_verify_partialENS_11PartialArgsE", "_ZN4mlav21mla_verify_partial_2sENS_11PartialArgsE"]
 
 
 @pytest.fixture(scope="module")
@@ -36,7 +36,7 @@ def test_no_mfma_hazards(asm, fn):
 def test_untracked_loads_awaited_before_use(asm, fn):
     insns, _ = asm_hazards.parse_function(asm, fn)
     loads = [x for x in insns if x.inline_asm and x.op.startswith("global_load_dword")]
-    assert len(loads) >= 3  # the prologue's slot indices were found
+    assert len(loads) >= 2  # the prologue's slot indices were found
     problems = asm_hazards.check_untracked_loads(insns)
     assert not problems, "\n".join(problems[:20])
 
