@@ -762,9 +762,13 @@ void mla_verify_partial(PartialArgs p) {
 // flight, so the partials stream at memory speed.  Each wave also forms the
 // merge weights itself: M = max_s lse_s, w_s = exp(lse_s - M) / sum_s exp(lse_s - M).
 // PartT is __bf16 for the library's own workspace, float for caller partials.
-constexpr int kMergeThreads = 256;
-constexpr int kMergeGroups = kMergeThreads / 64;  // split groups
 constexpr int kMergeUnroll = 8;
+// Split groups per workgroup (64 threads each): 4 in general; 16 when a call has few rows and many
+// splits, so that a row's many partials are read with more loads in flight (a decode step has 64
+// rows); with few splits the larger workgroup only costs launch and reduction time.
+constexpr int kMergeGroupsFew = 16;
+constexpr int kMergeFewRows = 512;      // fewer rows per call than this ...
+constexpr int kMergeManySplits = 64;    // ... and at least this many splits: kMergeGroupsFew
 
 // Eight consecutive partial values: loaded raw (so that a batch of loads is in flight at
 // once), widened to fp32 when used.
@@ -1097,8 +1101,8 @@ struct Raw8<__bf16> {
   }
 };
 
-template <typename PartT>
-__global__ __launch_bounds__(kMergeThreads) void mla_verify_merge_kernel(MergeArgs p) {
+template <typename PartT, int kMergeGroups>
+__global__ __launch_bounds__(64 * kMergeGroups) void mla_verify_merge_kernel(MergeArgs p) {
   __shared__ float group_sum[kMergeGroups - 1][64][8];
   const int tid = threadIdx.x, lane = tid & 63;
   const int rows_per_b = p.max_q_len * p.heads;
@@ -1193,10 +1197,15 @@ hipError_t launch_partial(const PartialArgs& a, hipStream_t stream) {
 
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream) {
   const int64_t rows = (int64_t)a.batch * a.max_q_len * a.heads;  // one workgroup per row
-  if (a.part_fp32)
-    hipLaunchKernelGGL(mla_verify_merge_kernel<float>, dim3((unsigned)rows), dim3(kMergeThreads), 0, stream, a);
+  const bool few = rows < kMergeFewRows && a.nsplit >= kMergeManySplits;
+  if (a.part_fp32 && few)
+    hipLaunchKernelGGL((mla_verify_merge_kernel<float, kMergeGroupsFew>), dim3((unsigned)rows), dim3(64 * kMergeGroupsFew), 0, stream, a);
+  else if (a.part_fp32)
+    hipLaunchKernelGGL((mla_verify_merge_kernel<float, 4>), dim3((unsigned)rows), dim3(256), 0, stream, a);
+  else if (few)
+    hipLaunchKernelGGL((mla_verify_merge_kernel<__bf16, kMergeGroupsFew>), dim3((unsigned)rows), dim3(64 * kMergeGroupsFew), 0, stream, a);
   else
-    hipLaunchKernelGGL(mla_verify_merge_kernel<__bf16>, dim3((unsigned)rows), dim3(kMergeThreads), 0, stream, a);
+    hipLaunchKernelGGL((mla_verify_merge_kernel<__bf16, 4>), dim3((unsigned)rows), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

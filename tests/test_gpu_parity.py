@@ -171,9 +171,9 @@ def test_overflow_to_inf_fallback_rows(api):
     _check(api, x, 1, "overflow-inf")
 
 
-def test_merge_kernel_alone(api):
+@pytest.mark.parametrize("S", [6, 80])  # 80: few rows and many splits take the 16-group merge
+def test_merge_kernel_alone(api, S):
     x = I.make_custom(np.random.default_rng(36), [400, 37], [5, 3], 6, 1000)
-    S = 6
     ref_o, ref_l, o_part, l_part = oracle.verify_attention_split(
         x.q, x.pool(), x.slot_idx, x.seq_lens, x.q_lens, x.scale, S, return_partials=True)
     B, H, maxq = 2, 6, 5
