@@ -395,6 +395,23 @@ def main():
     flops, kv_bytes, alg_bytes = algorithmic_counts(x)
     p95 = times_us[min(len(times_us) - 1, int(0.95 * len(times_us)))]
     k1_tflops = flops / (k1_us * 1e-6) / 1e12 if k1_us == k1_us else None
+    # kernel 1's roof: bf16 MFMA above the ridge (flop per byte of the call's algorithmic bytes),
+    # HBM below it (q_len = 1 decode: H flop/B ~ 121 against a ridge of 312)
+    ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBPS * 1e9)
+    k1_kernel = "mla_verify_partial_2s" if x.heads * int(x.q_lens.max()) <= 64 else "mla_verify_partial"
+    if flops / alg_bytes >= ridge:
+        roofline = {"bound": "mfma", "kernel": k1_kernel,
+                    "achieved": round(k1_tflops, 1) if k1_tflops else None, "peak": PEAK_BF16_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(k1_tflops / PEAK_BF16_TFLOPS, 4) if k1_tflops else None,
+                    "traffic": measured_traffic(w.name), "traffic_unit": "bytes/launch",
+                    "flops_per_launch": flops}
+    else:
+        k1_gbps = alg_bytes / (k1_us * 1e-6) / 1e9 if k1_us == k1_us else None
+        roofline = {"bound": "hbm", "kernel": k1_kernel,
+                    "achieved": round(k1_gbps, 1) if k1_gbps else None, "peak": PEAK_HBM_GBPS,
+                    "unit": "GB/s", "frac": round(k1_gbps / PEAK_HBM_GBPS, 4) if k1_gbps else None,
+                    "traffic": measured_traffic(w.name), "traffic_unit": "bytes/launch",
+                    "bytes_per_launch": alg_bytes}
     res = {
         "metric": METRIC,
         "value": round(us, 3),
@@ -422,11 +439,7 @@ def main():
         "tflops_frac_of_mfma": round(flops / (us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "partial_kernel_us": round(k1_us, 3) if k1_us == k1_us else None,
         "parity_sampled": {"rows": len(rows), "max_abs_err_out": err_o, "max_abs_err_lse": err_l},
-        "roofline": {"bound": "mfma", "kernel": "mla_verify_partial",
-                     "achieved": round(k1_tflops, 1) if k1_tflops else None, "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(k1_tflops / PEAK_BF16_TFLOPS, 4) if k1_tflops else None,
-                     "traffic": measured_traffic(w.name), "traffic_unit": "bytes/launch",
-                     "flops_per_launch": flops},
+        "roofline": roofline,
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(x, args.cpu_budget)
