@@ -763,12 +763,14 @@ void mla_verify_partial(PartialArgs p) {
 // merge weights itself: M = max_s lse_s, w_s = exp(lse_s - M) / sum_s exp(lse_s - M).
 // PartT is __bf16 for the library's own workspace, float for caller partials.
 constexpr int kMergeUnroll = 8;
-// Split groups per workgroup (64 threads each): 4 in general; 16 when a call has few rows and many
-// splits, so that a row's many partials are read with more loads in flight (a decode step has 64
-// rows); with few splits the larger workgroup only costs launch and reduction time.
+// Split groups per workgroup (64 threads each): 4 in general.  A call with few rows and many
+// splits (a decode step has 64 rows) takes the column-sliced form below, which spreads a row over
+// four workgroups, or, past the split count that form holds in LDS, 16 groups, so that a row's
+// many partials are read with more loads in flight; with few splits or many rows either only
+// costs launch and reduction time.
 constexpr int kMergeGroupsFew = 16;
 constexpr int kMergeFewRows = 512;      // fewer rows per call than this ...
-constexpr int kMergeManySplits = 64;    // ... and at least this many splits: kMergeGroupsFew
+constexpr int kMergeManySplits = 64;    // ... and at least this many splits: the forms for few rows
 
 // Eight consecutive partial values: loaded raw (so that a batch of loads is in flight at
 // once), widened to fp32 when used.
@@ -1186,6 +1188,118 @@ __global__ __launch_bounds__(64 * kMergeGroups) void mla_verify_merge_kernel(Mer
   }
 }
 
+// Kernel 2 for calls with few rows and many splits (a decode step: 64 rows, each with up to
+// hundreds of partials): one workgroup of 256 threads per (request, row, 128-column slice), so
+// that four times as many workgroups share the reads of a row.  The workgroup forms the merge
+// weights once, from block-wide max and sum over the row's LSEs, and keeps them in LDS; thread t
+// covers columns 8*(t%16) of its slice over the splits t/16, t/16 + 16, ...; the 16 partial sums
+// are added through LDS.
+constexpr int kSliceCols = 128;                          // output columns per workgroup
+constexpr int kSliceThreads = kSliceCols / 8;            // threads per split group
+constexpr int kSliceGroups = 256 / kSliceThreads;        // split groups per workgroup
+constexpr int kSliceMaxSplits = 1024;                    // weights held in LDS
+constexpr int kSliceLsePerThread = kSliceMaxSplits / 256;
+
+template <typename PartT>
+__global__ __launch_bounds__(256) void mla_verify_merge_sliced(MergeArgs p) {
+  __shared__ float wts[kSliceMaxSplits];
+  __shared__ float wred[2][4];
+  __shared__ float gsum[kSliceGroups - 1][kSliceThreads][8];
+  constexpr int kSlices = kDv / kSliceCols;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int slice = (int)(blockIdx.x % kSlices);
+  const int64_t row_id = blockIdx.x / kSlices;
+  const int rows_per_b = p.max_q_len * p.heads;
+  const int b = (int)(row_id / rows_per_b);
+  const int r = (int)(row_id - (int64_t)b * rows_per_b);
+  if (b >= p.batch) return;
+  const int Q = clamped_q(p.q_lens, p.seq_lens, b, p.max_q_len);
+  if (r >= Q * p.heads) return;  // uniform over the workgroup
+  const int ns = p.use_all_splits ? p.nsplit : split_count(p.seq_lens[b], p.nsplit, p.min_tiles);
+  int64_t qo = 0;
+  for (int i = 0; i < b; ++i) qo += clamped_q(p.q_lens, p.seq_lens, i, p.max_q_len);
+
+  const int64_t base = (int64_t)b * p.nsplit * p.rows_stride + r;  // (b, s=0, r)
+  const float* lse_s = p.lse_part + base;
+  const int c = tid % kSliceThreads, sg = tid / kSliceThreads;
+  const PartT* src = (const PartT*)p.o_part + base * kDv + slice * kSliceCols + 8 * c;
+  const int64_t sstride = (int64_t)p.rows_stride * kDv;
+
+  // the row's LSEs (split tid + 256k), then the first batch of partial loads
+  float x[kSliceLsePerThread];
+#pragma unroll
+  for (int k = 0; k < kSliceLsePerThread; ++k) {
+    const int s = tid + 256 * k;
+    x[k] = s < ns ? lse_s[(int64_t)s * p.rows_stride] : -INFINITY;
+  }
+  Raw8<PartT> v[kMergeUnroll];
+  auto load_batch = [&](int s0) {  // splits past ns re-read split 0 (weight 0 below)
+#pragma unroll
+    for (int u = 0; u < kMergeUnroll; ++u) {
+      const int s = s0 + kSliceGroups * u;
+      v[u].load(src + (int64_t)(s < ns ? s : 0) * sstride);
+    }
+  };
+  load_batch(sg);
+
+  // M = max_s lse_s, Z = sum_s exp(lse_s - M), w_s = exp(lse_s - M) / Z, while the partials load
+  float m = x[0];
+#pragma unroll
+  for (int k = 1; k < kSliceLsePerThread; ++k) m = fmaxf(m, x[k]);
+  m = wave_max(m);
+  if (lane == 0) wred[0][wv] = m;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(wred[0][0], wred[0][1]), fmaxf(wred[0][2], wred[0][3]));
+  const float Mref = (M == -INFINITY) ? 0.f : M;
+  float e[kSliceLsePerThread], z = 0.f;
+#pragma unroll
+  for (int k = 0; k < kSliceLsePerThread; ++k) {
+    e[k] = x[k] > -INFINITY ? __expf(x[k] - Mref) : 0.f;
+    z += e[k];
+  }
+  z = wave_sum(z);
+  if (lane == 0) wred[1][wv] = z;
+  __syncthreads();
+  const float Z = (wred[1][0] + wred[1][1]) + (wred[1][2] + wred[1][3]);
+  const float invZ = Z > 0.f ? 1.0f / Z : 0.f;
+#pragma unroll
+  for (int k = 0; k < kSliceLsePerThread; ++k) {
+    const int s = tid + 256 * k;
+    if (s < ns) wts[s] = e[k] * invZ;
+  }
+  __syncthreads();
+
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int s0 = sg;;) {
+#pragma unroll
+    for (int u = 0; u < kMergeUnroll; ++u) {
+      const int s = s0 + kSliceGroups * u;
+      const float ws = s < ns ? wts[s] : 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] += ws * v[u].get(j);
+    }
+    s0 += kSliceGroups * kMergeUnroll;
+    if (s0 >= ns) break;
+    load_batch(s0);
+  }
+  if (sg > 0)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) gsum[sg - 1][c][j] = acc[j];
+  __syncthreads();
+  if (sg == 0) {
+#pragma unroll
+    for (int g = 0; g < kSliceGroups - 1; ++g)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] += gsum[g][c][j];
+    const int64_t orow = qo * p.heads + r;
+    bf16x8 ov;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ov[j] = (__bf16)acc[j];
+    *(bf16x8*)(p.out + orow * kDv + slice * kSliceCols + 8 * c) = ov;
+    if (slice == 0 && tid == 0) p.lse[orow] = Z > 0.f ? Mref + __logf(Z) : -INFINITY;
+  }
+}
+
 hipError_t launch_partial(const PartialArgs& a, hipStream_t stream) {
   const int64_t grid = (int64_t)a.batch * a.nsplit * a.row_groups;
   if (a.streams == 2)
@@ -1198,7 +1312,13 @@ hipError_t launch_partial(const PartialArgs& a, hipStream_t stream) {
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream) {
   const int64_t rows = (int64_t)a.batch * a.max_q_len * a.heads;  // one workgroup per row
   const bool few = rows < kMergeFewRows && a.nsplit >= kMergeManySplits;
-  if (a.part_fp32 && few)
+  if (few && a.nsplit <= kSliceMaxSplits) {
+    const dim3 grid((unsigned)(rows * (kDv / kSliceCols)));
+    if (a.part_fp32)
+      hipLaunchKernelGGL(mla_verify_merge_sliced<float>, grid, dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL(mla_verify_merge_sliced<__bf16>, grid, dim3(256), 0, stream, a);
+  } else if (a.part_fp32 && few)
     hipLaunchKernelGGL((mla_verify_merge_kernel<float, kMergeGroupsFew>), dim3((unsigned)rows), dim3(64 * kMergeGroupsFew), 0, stream, a);
   else if (a.part_fp32)
     hipLaunchKernelGGL((mla_verify_merge_kernel<float, 4>), dim3((unsigned)rows), dim3(256), 0, stream, a);

@@ -171,7 +171,9 @@ def test_overflow_to_inf_fallback_rows(api):
     _check(api, x, 1, "overflow-inf")
 
 
-@pytest.mark.parametrize("S", [6, 80])  # 80: few rows and many splits take the 16-group merge
+# with 60 rows: 6 splits take the 4-group merge, 80 and 300 the column-sliced one (300: more
+# splits than threads), 1100 (more than the sliced form holds in LDS) the 16-group one
+@pytest.mark.parametrize("S", [6, 80, 300, 1100])
 def test_merge_kernel_alone(api, S):
     x = I.make_custom(np.random.default_rng(36), [400, 37], [5, 3], 6, 1000)
     ref_o, ref_l, o_part, l_part = oracle.verify_attention_split(
