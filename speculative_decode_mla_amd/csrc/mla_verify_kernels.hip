@@ -988,10 +988,9 @@ void mla_verify_partial_2s(PartialArgs p) {
   // ---- merge of the two streams, then the partial write (one partial per split, as in the
   // 128-row form).  Each stream's sums and accumulators are relative to its own reference m_s;
   // with m = max(m_0, m_1) and a_s = 2^(m_s - m), the split's are l = sum_s a_s l_s and
-  // O = sum_s a_s O_s.  Stream 1 hands over its per-row (m, l, l_exact) and, in two column halves
-  // (to fit beside the staging rows), its accumulators through LDS; stream 0 combines, normalises
-  // and stores.  A row where either stream's sum outgrew its reference is redone exactly over
-  // the whole split.
+  // O = sum_s a_s O_s.  The per-row (m, l, l_exact) of every wave go through LDS; the
+  // accumulators are combined column block by column block by both streams (below).  A row where
+  // either stream's sum outgrew its reference is redone exactly over the whole split.
   const float lt = pair_sum(st.l_run);
   const float le = pair_sum(st.l_exact);
   __syncthreads();  // every wave is done with the ring and the P exchange buffers
@@ -1026,62 +1025,84 @@ void mla_verify_partial_2s(PartialArgs p) {
         co.lex > 0.f ? (co.m + __builtin_amdgcn_logf(co.lex)) * kLn2 : -INFINITY;
 
   typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-  lds_char* stage = smem + (w & 1) * kStageBytes;               // stream 0's staging rows
-  lds_char* dump = smem + 2 * kStageBytes + (w & 1) * 32 * 1024;  // stream 1's accumulators, one half
-  static_assert(2 * kStageBytes + 2 * 32 * 1024 <= kRing * kTileBytes, "staging and hand-over fit the ring");
+  // Both streams combine: in phase ph (column blocks 4ph .. 4ph+3 of the wave pair's 256 columns)
+  // stream 0 combines blocks 4ph, 4ph+1 and stream 1 blocks 4ph+2, 4ph+3, each after taking the
+  // other stream's accumulators for its blocks through LDS; the bf16 rows meet in one staging area
+  // per wave pair, and each stream stores 32 of its 64 rows.
+  lds_char* stage = smem + (w & 1) * kStageBytes;
+  constexpr int kDumpBytes = 16 * 1024;  // two column blocks, own and partner rows: 64 floats a lane
+  static_assert(2 * kStageBytes + kWaves * kDumpBytes <= kRing * kTileBytes, "staging and hand-over fit the ring");
+  lds_char* dump_mine = smem + 2 * kStageBytes + w * kDumpBytes;
+  const lds_char* dump_other = smem + 2 * kStageBytes + (w ^ 2) * kDumpBytes;
+  // O = (O_0 a_0 + O_1 a_1) / l, with the division folded into the weights
+  const float own_mine = (stream == 0 ? co.a0 : co.a1) * co.inv, own_other = (stream == 0 ? co.a1 : co.a0) * co.inv;
+  const float par_mine = (stream == 0 ? cp.a0 : cp.a1) * cp.inv, par_other = (stream == 0 ? cp.a1 : cp.a0) * cp.inv;
+  auto epilogue_phase = [&](auto ph_c, auto stream_c) __attribute__((always_inline)) {
+    constexpr int ph = decltype(ph_c)::value, S = decltype(stream_c)::value;
+    constexpr int give = 4 * ph + (S == 0 ? 2 : 0), keep = 4 * ph + (S == 0 ? 0 : 2);
 #pragma unroll
-  for (int ph = 0; ph < 2; ++ph) {
-    if (stream == 1) {  // column blocks 4ph .. 4ph+3: own and partner rows, 4 values per (c, q4)
+    for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x16& oo = o_own[give + cc];
+        const f32x16& op = o_par[give + cc];
+        const f32x4 vo = {acc_read(oo[4 * q4]), acc_read(oo[4 * q4 + 1]), acc_read(oo[4 * q4 + 2]), acc_read(oo[4 * q4 + 3])};
+        const f32x4 vp = {acc_read(op[4 * q4]), acc_read(op[4 * q4 + 1]), acc_read(op[4 * q4 + 2]), acc_read(op[4 * q4 + 3])};
+        const int j = (cc * 4 + q4) * 2;
+        *(__attribute__((address_space(3))) f32x4*)(dump_mine + (j * 64 + lane) * 16) = vo;
+        *(__attribute__((address_space(3))) f32x4*)(dump_mine + ((j + 1) * 64 + lane) * 16) = vp;
+      }
+    __syncthreads();  // both streams' hand-over halves are in LDS
+    f32x4 dd[16];     // all reads go out before any is used
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const f32x16& oo = o_own[4 * ph + c];
-          const f32x16& op = o_par[4 * ph + c];
-          const f32x4 vo = {acc_read(oo[4 * q4]), acc_read(oo[4 * q4 + 1]), acc_read(oo[4 * q4 + 2]), acc_read(oo[4 * q4 + 3])};
-          const f32x4 vp = {acc_read(op[4 * q4]), acc_read(op[4 * q4 + 1]), acc_read(op[4 * q4 + 2]), acc_read(op[4 * q4 + 3])};
-          const int j = (c * 4 + q4) * 2;
-          *(__attribute__((address_space(3))) f32x4*)(dump + (j * 64 + lane) * 16) = vo;
-          *(__attribute__((address_space(3))) f32x4*)(dump + ((j + 1) * 64 + lane) * 16) = vp;
+    for (int j = 0; j < 16; ++j) dd[j] = *(const __attribute__((address_space(3))) f32x4*)(dump_other + (j * 64 + lane) * 16);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x16& oo = o_own[keep + cc];
+        const f32x16& op = o_par[keep + cc];
+        const int j = (cc * 4 + q4) * 2;
+        const int cb = (32 * (keep + cc) + 8 * q4 + 4 * hi) * 2;
+        bf16x4 vo, vp;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          vo[e] = (__bf16)(acc_read(oo[4 * q4 + e]) * own_mine + dd[j][e] * own_other);
+          vp[e] = (__bf16)(acc_read(op[4 * q4 + e]) * par_mine + dd[j + 1][e] * par_other);
         }
-    }
-    __syncthreads();  // the half of stream 1's accumulators is in LDS
-    if (stream == 0) {
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const f32x16& oo = o_own[4 * ph + c];
-          const f32x16& op = o_par[4 * ph + c];
-          const int j = (c * 4 + q4) * 2;
-          const f32x4 do_ = *(const __attribute__((address_space(3))) f32x4*)(dump + (j * 64 + lane) * 16);
-          const f32x4 dp = *(const __attribute__((address_space(3))) f32x4*)(dump + ((j + 1) * 64 + lane) * 16);
-          const int cb = (32 * (4 * ph + c) + 8 * q4 + 4 * hi) * 2;
-          bf16x4 vo, vp;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            vo[e] = (__bf16)((acc_read(oo[4 * q4 + e]) * co.a0 + do_[e] * co.a1) * co.inv);
-            vp[e] = (__bf16)((acc_read(op[4 * q4 + e]) * cp.a0 + dp[e] * cp.a1) * cp.inv);
-          }
-          *(__attribute__((address_space(3))) bf16x4*)(stage + lrow * kStageRowBytes + cb) = vo;
-          *(__attribute__((address_space(3))) bf16x4*)(stage + (32 + lrow) * kStageRowBytes + cb) = vp;
-        }
-    }
-    if (ph == 0) __syncthreads();  // stream 0 has read the first half before stream 1 writes the second
-  }
+        *(__attribute__((address_space(3))) bf16x4*)(stage + lrow * kStageRowBytes + cb) = vo;
+        *(__attribute__((address_space(3))) bf16x4*)(stage + (32 + lrow) * kStageRowBytes + cb) = vp;
+      }
+    if (ph == 0) __syncthreads();  // the hand-over area is read before phase 1 writes it again
+  };
   if (stream == 0) {
-    // stage rows 0..31 are this wave's rows, 32..63 its partner's; two rows per store instruction
+    epilogue_phase(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
+    epilogue_phase(std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{});
+  } else {
+    epilogue_phase(std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{});
+    epilogue_phase(std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{});
+  }
+  __syncthreads();  // both streams' columns are staged
+  {
+    // stage rows 0..31 are wave pair h's own rows, 32..63 its partner's; stream s stores rows
+    // 32s .. 32s+31, two rows per store instruction
     uint16_t* part_base = p.o_part + (int64_t)wi.bs * p.rows_pad * kDv + (w_uniform & 1) * (kDv / 2) + (lane & 31) * 8;
-#pragma unroll 4
-    for (int k = 0; k < 32; ++k) {
-      const int r = 2 * k + hi;
-      const i32x4 v = *(const __attribute__((address_space(3))) i32x4*)(stage + r * kStageRowBytes + (lane & 31) * 16);
+    const int rbase = 32 * (w_uniform >> 1);
+    i32x4 sv[16];  // all staged rows read first, then all stores
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+      sv[k] = *(const __attribute__((address_space(3))) i32x4*)(stage + (rbase + 2 * k + hi) * kStageRowBytes + (lane & 31) * 16);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int r = rbase + 2 * k + hi;
       const int grow = row0 + (r < 32 ? half * kRowsPerWave + r : (1 - half) * kRowsPerWave + r - 32);
-      if (grow < R) *(i32x4*)(part_base + (int64_t)grow * kDv) = v;
+      if (grow < R) *(i32x4*)(part_base + (int64_t)grow * kDv) = sv[k];
     }
   }
   if (any_redo) {
-    __syncthreads();  // (global writes of both halves are ordered by the barrier's release/acquire)
+    __syncthreads();  // (the global writes of all four waves are ordered by the barrier's release/acquire)
     if (stream == 0 && redo != 0) redo_rows_exact(p, wi, row0 + half * kRowsPerWave, (uint32_t)redo, 0, 1, wi.bs);
   }
 }
