@@ -14,6 +14,8 @@ struct mla_verify_s {
   int32_t row_groups;
   int32_t rows_pad;
   int32_t streams;    // kernel 1 form: 1 (128-row workgroups) or 2 (64-row workgroups, two key streams)
+  int32_t plan_ranges;  // 1: batches of 2..64 requests in the 128-row form use the range plan
+  int32_t workers;      // range plan: workers, one workgroup per row group each (CUs / row groups)
   uint16_t* o_part;  // bf16 [B, max_nsplit, rows_pad, 512]
   float* lse_part;  // [B, max_nsplit, rows_pad]
 };
@@ -67,6 +69,9 @@ int mla_verify_create(const mla_verify_config* cfg, mla_verify_handle* out) {
 
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return MLA_ERR_HIP;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    return MLA_ERR_HIP;
   const int64_t partial_rows = (int64_t)cfg->batch * cfg->max_nsplit * rows_pad;
   mla_verify_s* h = new (std::nothrow) mla_verify_s();
   if (h == nullptr) return MLA_ERR_OUT_OF_MEMORY;
@@ -75,6 +80,13 @@ int mla_verify_create(const mla_verify_config* cfg, mla_verify_handle* out) {
   h->row_groups = (int32_t)row_groups;
   h->rows_pad = (int32_t)rows_pad;
   h->streams = streams;
+  // A batch in the 128-row form is spread over one workgroup per CU (one resident per CU), as
+  // `workers` workers of row_groups workgroups each (the range plan of kernel 1).
+  h->plan_ranges = streams == 1 && cfg->batch >= 2 && cfg->batch <= mlav::kRangeMaxBatch && row_groups <= cus;
+  // (a multiple of 8 from 8 workers on, so that each XCD takes the same share and holds at most
+  // 64 workers, one per lane of the planner's wave)
+  const int64_t workers = cus / row_groups;
+  h->workers = h->plan_ranges ? (int32_t)(workers >= 8 ? workers & ~int64_t(7) : workers) : 0;
   int st = hip_status(hipMalloc((void**)&h->o_part, (size_t)partial_rows * mlav::kDv * sizeof(uint16_t)));
   if (st == MLA_OK) st = hip_status(hipMalloc((void**)&h->lse_part, (size_t)partial_rows * sizeof(float)));
   if (st != MLA_OK) {
@@ -119,6 +131,8 @@ int launch_partials(mla_verify_handle h, const void* q, const void* kv_pool, con
   pa.rows_pad = h->rows_pad;
   pa.min_tiles = kMinTilesPerSplit;
   pa.streams = h->streams;
+  pa.plan_ranges = h->plan_ranges;
+  pa.workers = h->workers;
   pa.scale_log2 = c.sm_scale * 1.4426950408889634f;
   return mlav::launch_partial(pa, s) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
@@ -158,6 +172,8 @@ int mla_verify_run(mla_verify_handle h, const void* q, const void* kv_pool, cons
   ma.min_tiles = kMinTilesPerSplit;
   ma.use_all_splits = 0;
   ma.part_fp32 = 0;
+  ma.plan_ranges = h->plan_ranges;
+  ma.workers = h->workers;
   return mlav::launch_merge(ma, s) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
@@ -185,6 +201,8 @@ int mla_verify_merge(const float* o_part, const float* lse_part, const int32_t* 
   ma.min_tiles = 1;
   ma.use_all_splits = 1;
   ma.part_fp32 = 1;
+  ma.plan_ranges = 0;
+  ma.workers = 0;
   return hip_status(mlav::launch_merge(ma, static_cast<hipStream_t>(stream))) == MLA_OK ? MLA_OK : MLA_ERR_HIP;
 }
 

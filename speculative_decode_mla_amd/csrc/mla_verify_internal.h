@@ -15,6 +15,7 @@ constexpr int kRowsPerWave = 32;     // (token, head) rows owned by one wave
 constexpr int kRowsPerGroup = kWaves * kRowsPerWave;  // rows per workgroup: 128
 constexpr int kTileKeys = 32;        // keys gathered into LDS per step (one MFMA block)
 constexpr int kRowsPerGroup2s = 2 * kRowsPerWave;  // rows per workgroup in the two-stream form: 64
+constexpr int kRangeMaxBatch = 64;   // the range plan holds one request per lane of a wave
 
 // Kernel 1: one workgroup per (request, split, 128-row group).
 struct PartialArgs {
@@ -30,6 +31,8 @@ struct PartialArgs {
   int32_t rows_pad;          // row_groups * 128
   int32_t min_tiles;         // fewest 32-key tiles a split is given (caps the split count)
   int32_t streams;           // 1: 128-row workgroups; 2: 64-row workgroups over two key streams
+  int32_t plan_ranges;       // 1: range plan (128-row form, 2..kRangeMaxBatch requests); 0: splits per request
+  int32_t workers;           // range plan: workers (each one workgroup per row group)
   float scale_log2;          // sm_scale * log2(e)
 };
 
@@ -44,6 +47,8 @@ struct MergeArgs {
   int32_t batch, heads, max_q_len, nsplit, rows_stride, min_tiles;
   int32_t use_all_splits;    // 1: merge all nsplit partials; 0: only the splits kernel 1 filled
   int32_t part_fp32;         // 1: o_part holds fp32 values; 0: bf16
+  int32_t plan_ranges;       // 1: kernel 1 ran the range plan with `workers` workers (partials per request from it)
+  int32_t workers;
 };
 
 // KV compaction: dst[dst_first + j] = src[slot_idx[j]] (whole 1152-B rows), j < n_rows.

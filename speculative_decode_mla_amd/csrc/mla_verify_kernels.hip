@@ -287,6 +287,177 @@ __device__ __forceinline__ bool decode_work(const PartialArgs& p, int wg, int ro
   return true;
 }
 
+// ---- Range plan for a batch of requests (2 .. kRangeMaxBatch requests) ------------------------------
+// Splitting a ragged batch per request gives every request the same number of splits: a short
+// request's workgroups finish early, a long one's late, and every split pays the fixed cost of
+// staging q and writing a partial.  The range plan instead lays the 32-key tiles of all requests, in
+// request order, out as one sequence of T tiles (a request without rows contributes none) and cuts
+// it into chunks of C consecutive tiles, one per worker (a worker is one workgroup per 128-row
+// group).  A chunk may end inside a request and carry on into the next ones: it holds one piece per
+// request it touches, and each piece is one workgroup.  A request's partial s is its piece of chunk
+// floor(J_b / C) + s (J_b: the request's first tile in the sequence), so every partial covers a
+// contiguous key range.  C starts from an even share of T per worker and is raised only as far as
+// needed to keep every request within nsplit chunks.
+//
+// Dispatch order does the balancing: the workers of XCD x are those with o = x (mod 8), and the
+// workgroups of XCD x run its pieces in rounds, round k holding the k-th largest piece of each of
+// its chunks; so every CU starts on the largest piece of a chunk, and the smaller pieces go to
+// whichever CUs free up first.  The grid is sized for the most pieces a batch can have; workgroups
+// past the actual pieces exit after the decode.  Kernel 1 and the merge both derive the plan from
+// seq_lens and q_lens on the device, so it needs no host step and the call stays capture-safe.
+// Tile counts are 32-bit: T stays below 2^31 for any batch whose slot list fits in memory.
+
+struct RequestScan {  // lane b < batch holds request b; lanes past the batch hold zeros
+  int L, Q, tiles;    // keys, clamped draft tokens, tiles with work (0 when the request has no rows)
+  int J;              // first tile of the request in the batch's tile sequence
+  int qo;             // first (draft token) row of the request: prefix sum of the clamped q_lens
+  int64_t ko;         // first key of the request in slot_idx: prefix sum of seq_lens
+};
+
+__device__ __forceinline__ int wave_excl_scan(int v, int lane) {
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  return x - v;
+}
+
+__device__ __forceinline__ RequestScan scan_requests(const int32_t* seq_lens, const int32_t* q_lens, int batch,
+                                                     int max_q) {
+  const int lane = threadIdx.x & 63;
+  RequestScan r;
+  r.L = lane < batch ? seq_lens[lane] : 0;
+  r.Q = lane < batch ? clamped_q(q_lens, seq_lens, lane, max_q) : 0;
+  r.tiles = r.Q > 0 ? (r.L + kTileKeys - 1) / kTileKeys : 0;
+  r.J = wave_excl_scan(r.tiles, lane);
+  r.qo = wave_excl_scan(r.Q, lane);
+  int64_t x = r.L;  // 64-bit prefix of seq_lens
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int64_t y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  r.ko = x - r.L;
+  return r;
+}
+
+// Does every request lie within nsplit chunks of C tiles?
+__device__ __forceinline__ bool chunks_fit(const RequestScan& r, int C, int nsplit) {
+  const bool ok = r.tiles == 0 || (r.J + r.tiles - 1) / C - r.J / C + 1 <= nsplit;
+  return __all(ok) != 0;
+}
+
+// The chunk length C (tiles per worker); the same value in every lane and every workgroup.
+__device__ __forceinline__ int range_chunk(const RequestScan& r, int nsplit, int workers, int min_tiles) {
+  const int T = __builtin_amdgcn_readlane(r.J + r.tiles, 63);
+  if (T <= 0) return 1;
+  int C = (T + workers - 1) / workers;
+  if (C < min_tiles) C = min_tiles;
+  if (chunks_fit(r, C, nsplit)) return C;
+  int maxt = r.tiles;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) maxt = max(maxt, __shfl_xor(maxt, o));
+  const int C1 = (maxt + nsplit - 1) / nsplit;  // the fewest tiles per chunk for the longest request
+  if (C1 > C) {
+    C = C1;
+    if (chunks_fit(r, C, nsplit)) return C;
+  }
+  // A request of t tiles meets at most floor((t - 1) / C) + 2 chunks, so this always fits;
+  // with one split per request, one chunk holds the whole batch.
+  if (nsplit < 2) return T;
+  const int C2 = (maxt + nsplit - 2) / (nsplit - 1);
+  return C2 > C ? C2 : C;
+}
+
+// Requests (lanes) with tiles in chunk [lo, hi).
+__device__ __forceinline__ uint64_t chunk_requests(const RequestScan& r, int lo, int hi) {
+  return __ballot(r.tiles > 0 && r.J < hi && r.J + r.tiles > lo);
+}
+
+// Grid of the range plan: per pool (XCD), room for every worker's first piece plus one piece per
+// request boundary, times the row groups.
+__host__ __device__ __forceinline__ int range_pools(int workers) { return (workers & 7) == 0 ? 8 : 1; }
+__host__ __device__ __forceinline__ int64_t range_grid(int workers, int row_groups, int batch) {
+  const int pools = range_pools(workers);
+  return (int64_t)pools * (workers / pools + batch - 1) * row_groups;
+}
+
+// Decode a workgroup id of the range plan; false if it has nothing to do.
+__device__ __forceinline__ bool decode_piece(const PartialArgs& p, int wg, WorkItem& wi) {
+  const int lane = threadIdx.x & 63;
+  const RequestScan r = scan_requests(p.seq_lens, p.q_lens, p.batch, p.max_q_len);
+  const int C = __builtin_amdgcn_readfirstlane(range_chunk(r, p.nsplit, p.workers, p.min_tiles));
+  const int T = __builtin_amdgcn_readlane(r.J + r.tiles, 63);
+  const int pools = range_pools(p.workers), per_pool = p.workers / pools;
+  const int x = pools == 8 ? (wg & 7) : 0, kk = pools == 8 ? (wg >> 3) : wg;
+  int j = kk / p.row_groups;
+  const int g = kk - j * p.row_groups;
+  // pieces of each of the pool's workers (worker x + pools*i in lane i)
+  int npieces = 0;
+  for (int i = 0; i < per_pool; ++i) {
+    const int o = x + pools * i;
+    if ((int64_t)o * C >= T) break;
+    const int lo = o * C, hi = lo + (C < T - lo ? C : T - lo);
+    const int n = __popcll(chunk_requests(r, lo, hi));
+    if (lane == (i & 63) && i < 64) npieces = n;
+  }
+  // round k holds the k-th largest piece of each chunk with more than k pieces, workers in order
+  int o = -1, k = 0;
+  for (;; ++k) {
+    const uint64_t has = __ballot(lane < per_pool && npieces > k);
+    if (has == 0) return false;
+    const int cnt = __popcll(has);
+    if (j < cnt) {
+      uint64_t m = has;
+      for (int t = 0; t < j; ++t) m &= m - 1;
+      o = x + pools * __builtin_ctzll(m);
+      break;
+    }
+    j -= cnt;
+  }
+  const int lo = o * C, hi = lo + (C < T - lo ? C : T - lo);
+  const uint64_t reqs = chunk_requests(r, lo, hi);
+  // the k-th largest piece of the chunk (ties in request order)
+  const int size = min(hi, r.J + r.tiles) - max(lo, r.J);
+  int rank = 0;
+  for (uint64_t m = reqs; m != 0; m &= m - 1) {
+    const int b2 = __builtin_ctzll(m);
+    const int s2 = __builtin_amdgcn_readlane(size, b2);
+    rank += (s2 > size || (s2 == size && b2 < lane)) ? 1 : 0;
+  }
+  const uint64_t pick = __ballot(((reqs >> lane) & 1) != 0 && rank == k);
+  const int b = __builtin_ctzll(pick);
+  wi.b = b;
+  wi.g = g;
+  wi.L = __builtin_amdgcn_readlane(r.L, b);
+  wi.Q = __builtin_amdgcn_readlane(r.Q, b);
+  wi.R = wi.Q * p.heads;
+  if (g * kRowsPerGroup >= wi.R) return false;
+  const int J = __builtin_amdgcn_readlane(r.J, b);
+  const int tiles = __builtin_amdgcn_readlane(r.tiles, b);
+  wi.s = o - J / C;
+  wi.bs = b * p.nsplit + wi.s;
+  wi.t_begin = (lo > J ? lo : J) - J;
+  wi.t_end = (hi < J + tiles ? hi : J + tiles) - J;
+  wi.qo = __builtin_amdgcn_readlane(r.qo, b);
+  const uint32_t ko_lo = __builtin_amdgcn_readlane((int)(uint32_t)r.ko, b);
+  const uint32_t ko_hi = __builtin_amdgcn_readlane((int)(r.ko >> 32), b);
+  wi.ko = (int64_t)(((uint64_t)ko_hi << 32) | ko_lo);
+  return true;
+}
+
+// Number of partials of request b in the range plan (b uniform, b < batch).
+__device__ __forceinline__ int range_pieces(const int32_t* seq_lens, const int32_t* q_lens, int batch, int max_q,
+                                            int nsplit, int workers, int min_tiles, int b) {
+  const RequestScan r = scan_requests(seq_lens, q_lens, batch, max_q);
+  const int C = range_chunk(r, nsplit, workers, min_tiles);
+  const int J = __builtin_amdgcn_readlane(r.J, b);
+  const int tiles = __builtin_amdgcn_readlane(r.tiles, b);
+  return tiles > 0 ? (J + tiles - 1) / C - J / C + 1 : 0;
+}
+
 // Exact recomputation of rows whose fixed-reference row sum reached
 // kRowSumLimit (scores far above the max of the split's first tile): one row at
 // a time across the whole wave, with a running max and a rescale at every key,
@@ -410,14 +581,13 @@ __device__ __forceinline__ void mask_tile(f32x16& s, int key0, int limit) {
 
 }  // namespace
 
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
-void mla_verify_partial(PartialArgs p) {
+// Kernel 1's work on one item: request wi.b, its tiles [t_begin, t_end), the rows of group wi.g;
+// writes partial wi.bs of those rows.
+__device__ __forceinline__ void partial_item(const PartialArgs& p, const WorkItem& wi) {
   __shared__ __attribute__((aligned(1024))) char smem_raw[kRing * kTileBytes + kXchgBytes];
   lds_char* smem = (lds_char*)smem_raw;
   lds_char* xchg = smem + kRing * kTileBytes;  // [2][kWaves][2 KiB]: bf16 P of each wave, double-buffered
 
-  WorkItem wi;
-  if (!decode_work(p, blockIdx.x, kRowsPerGroup, wi)) return;
   const int L = wi.L, Q = wi.Q, H = p.heads, R = wi.R;
   const int ntiles = wi.t_end - wi.t_begin;
 
@@ -753,6 +923,23 @@ void mla_verify_partial(PartialArgs p) {
   if (any_redo) {
     __syncthreads();  // (global writes of both halves are ordered by the barrier's release/acquire)
     if (redo != 0) redo_rows_exact(p, wi, row0 + w * kRowsPerWave, (uint32_t)redo, 0, 1, wi.bs);
+  }
+}
+
+// Kernel 1, 128-row form.  kRanges = false: one workgroup per (request, split, row group), splits
+// of equal length per request.  kRanges = true: the range plan above, one workgroup per (piece,
+// row group).
+template <bool kRanges>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+void mla_verify_partial(PartialArgs p) {
+  if constexpr (!kRanges) {
+    WorkItem wi;
+    if (!decode_work(p, blockIdx.x, kRowsPerGroup, wi)) return;
+    partial_item(p, wi);
+  } else {
+    WorkItem wi;
+    if (!decode_piece(p, blockIdx.x, wi)) return;
+    partial_item(p, wi);
   }
 }
 
@@ -1124,23 +1311,39 @@ struct Raw8<__bf16> {
   }
 };
 
-template <typename PartT, int kMergeGroups>
-__global__ __launch_bounds__(64 * kMergeGroups) void mla_verify_merge_kernel(MergeArgs p) {
-  __shared__ float group_sum[kMergeGroups - 1][64][8];
+// kRowsPerBlock > 1 (with one split group): one wave per row, kRowsPerBlock consecutive rows of a
+// request per workgroup.  That is the form for the range plan, whose requests have few partials
+// each: a row's work is then one wave's few loads, and the plan (partials per request, request
+// offsets) is derived once per wave.
+template <typename PartT, int kMergeGroups, int kRowsPerBlock = 1>
+__global__ __launch_bounds__(64 * kMergeGroups * kRowsPerBlock) void mla_verify_merge_kernel(MergeArgs p) {
+  static_assert(kMergeGroups == 1 || kRowsPerBlock == 1, "several rows per workgroup take one split group each");
+  __shared__ float group_sum[kMergeGroups > 1 ? kMergeGroups - 1 : 1][64][8];
   const int tid = threadIdx.x, lane = tid & 63;
   const int rows_per_b = p.max_q_len * p.heads;
-  const int b = (int)(blockIdx.x / rows_per_b);
-  const int r = (int)(blockIdx.x - (int64_t)b * rows_per_b);
+  const int blocks_per_b = (rows_per_b + kRowsPerBlock - 1) / kRowsPerBlock;
+  const int b = (int)(blockIdx.x / blocks_per_b);
+  const int r = (int)(blockIdx.x - (int64_t)b * blocks_per_b) * kRowsPerBlock + (kRowsPerBlock > 1 ? tid >> 6 : 0);
   if (b >= p.batch) return;
-  const int Q = clamped_q(p.q_lens, p.seq_lens, b, p.max_q_len);
-  if (r >= Q * p.heads) return;
-  const int ns = p.use_all_splits ? p.nsplit : split_count(p.seq_lens[b], p.nsplit, p.min_tiles);
+  int ns;
   int64_t qo = 0;
-  for (int i = 0; i < b; ++i) qo += clamped_q(p.q_lens, p.seq_lens, i, p.max_q_len);
+  if (p.plan_ranges) {
+    const RequestScan rq = scan_requests(p.seq_lens, p.q_lens, p.batch, p.max_q_len);
+    if (r >= __builtin_amdgcn_readlane(rq.Q, b) * p.heads) return;
+    const int C = range_chunk(rq, p.nsplit, p.workers, p.min_tiles);
+    const int J = __builtin_amdgcn_readlane(rq.J, b), tiles = __builtin_amdgcn_readlane(rq.tiles, b);
+    ns = (J + tiles - 1) / C - J / C + 1;  // (tiles > 0: the request has rows)
+    qo = __builtin_amdgcn_readlane(rq.qo, b);
+  } else {
+    const int Q = clamped_q(p.q_lens, p.seq_lens, b, p.max_q_len);
+    if (r >= Q * p.heads) return;
+    ns = p.use_all_splits ? p.nsplit : split_count(p.seq_lens[b], p.nsplit, p.min_tiles);
+    for (int i = 0; i < b; ++i) qo += clamped_q(p.q_lens, p.seq_lens, i, p.max_q_len);
+  }
 
   const int64_t base = (int64_t)b * p.nsplit * p.rows_stride + r;  // (b, s=0, r)
   const float* lse_s = p.lse_part + base;
-  const int c8 = tid & 63, sg = tid >> 6;
+  const int c8 = tid & 63, sg = kMergeGroups > 1 ? tid >> 6 : 0;
   const PartT* src = (const PartT*)p.o_part + base * kDv + 8 * c8;
   const int64_t sstride = (int64_t)p.rows_stride * kDv;
 
@@ -1191,21 +1394,24 @@ __global__ __launch_bounds__(64 * kMergeGroups) void mla_verify_merge_kernel(Mer
     if (s0 >= ns) break;
     load_batch(s0);
   }
-  if (sg > 0)
+  if constexpr (kMergeGroups > 1) {
+    if (sg > 0)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) group_sum[sg - 1][c8][j] = acc[j];
-  __syncthreads();
+      for (int j = 0; j < 8; ++j) group_sum[sg - 1][c8][j] = acc[j];
+    __syncthreads();
+    if (sg == 0)
+#pragma unroll
+      for (int g = 0; g < kMergeGroups - 1; ++g)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] += group_sum[g][c8][j];
+  }
   if (sg == 0) {
-#pragma unroll
-    for (int g = 0; g < kMergeGroups - 1; ++g)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) acc[j] += group_sum[g][c8][j];
     const int64_t orow = qo * p.heads + r;
     bf16x8 ov;
 #pragma unroll
     for (int j = 0; j < 8; ++j) ov[j] = (__bf16)acc[j];
     *((bf16x8*)(p.out + orow * kDv) + c8) = ov;
-    if (tid == 0) p.lse[orow] = Z > 0.f ? Mref + __logf(Z) : -INFINITY;
+    if (lane == 0) p.lse[orow] = Z > 0.f ? Mref + __logf(Z) : -INFINITY;
   }
 }
 
@@ -1236,7 +1442,10 @@ __global__ __launch_bounds__(256) void mla_verify_merge_sliced(MergeArgs p) {
   if (b >= p.batch) return;
   const int Q = clamped_q(p.q_lens, p.seq_lens, b, p.max_q_len);
   if (r >= Q * p.heads) return;  // uniform over the workgroup
-  const int ns = p.use_all_splits ? p.nsplit : split_count(p.seq_lens[b], p.nsplit, p.min_tiles);
+  const int ns = p.use_all_splits ? p.nsplit
+                 : p.plan_ranges ? range_pieces(p.seq_lens, p.q_lens, p.batch, p.max_q_len, p.nsplit, p.workers,
+                                                p.min_tiles, b)
+                                 : split_count(p.seq_lens[b], p.nsplit, p.min_tiles);
   int64_t qo = 0;
   for (int i = 0; i < b; ++i) qo += clamped_q(p.q_lens, p.seq_lens, i, p.max_q_len);
 
@@ -1322,15 +1531,27 @@ __global__ __launch_bounds__(256) void mla_verify_merge_sliced(MergeArgs p) {
 }
 
 hipError_t launch_partial(const PartialArgs& a, hipStream_t stream) {
+  if (a.plan_ranges) {
+    const int64_t grid = range_grid(a.workers, a.row_groups, a.batch);
+    hipLaunchKernelGGL(mla_verify_partial<true>, dim3((unsigned)grid), dim3(kWaves * 64), 0, stream, a);
+    return hipGetLastError();
+  }
   const int64_t grid = (int64_t)a.batch * a.nsplit * a.row_groups;
   if (a.streams == 2)
     hipLaunchKernelGGL(mla_verify_partial_2s, dim3((unsigned)grid), dim3(kWaves * 64), 0, stream, a);
   else
-    hipLaunchKernelGGL(mla_verify_partial, dim3((unsigned)grid), dim3(kWaves * 64), 0, stream, a);
+    hipLaunchKernelGGL(mla_verify_partial<false>, dim3((unsigned)grid), dim3(kWaves * 64), 0, stream, a);
   return hipGetLastError();
 }
 
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream) {
+  if (a.plan_ranges) {  // (bf16 partials of the library's workspace)
+    constexpr int kRowsPerBlock = 4;
+    const int64_t blocks = (int64_t)a.batch * ((a.max_q_len * a.heads + kRowsPerBlock - 1) / kRowsPerBlock);
+    hipLaunchKernelGGL((mla_verify_merge_kernel<__bf16, 1, kRowsPerBlock>), dim3((unsigned)blocks),
+                       dim3(64 * kRowsPerBlock), 0, stream, a);
+    return hipGetLastError();
+  }
   const int64_t rows = (int64_t)a.batch * a.max_q_len * a.heads;  // one workgroup per row
   const bool few = rows < kMergeFewRows && a.nsplit >= kMergeManySplits;
   if (few && a.nsplit <= kSliceMaxSplits) {
