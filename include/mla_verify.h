@@ -97,7 +97,11 @@ int mla_verify_create(const mla_verify_config* cfg, mla_verify_handle* out);
  *   nsplit   1 <= nsplit <= max_nsplit.  The keys of each request are divided
  *            into at most nsplit contiguous chunks; the result does not depend
  *            on nsplit beyond rounding.  Keep it constant across replays of a
- *            captured graph.
+ *            captured graph.  With 2..64 requests (and more than 64 rows per
+ *            request) the chunks are cut from the whole batch's key sequence so
+ *            that every CU gets the same share of work; a request's result then
+ *            depends on the other requests' lengths through where its chunks
+ *            fall, again only up to rounding.
  * The handle's workspace is reused by every call: calls on one handle must
  * not overlap (serialise them on one stream).  Distinct handles are independent.
  */
