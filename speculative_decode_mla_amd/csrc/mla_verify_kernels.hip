@@ -448,16 +448,6 @@ __device__ __forceinline__ bool decode_piece(const PartialArgs& p, int wg, WorkI
   return true;
 }
 
-// Number of partials of request b in the range plan (b uniform, b < batch).
-__device__ __forceinline__ int range_pieces(const int32_t* seq_lens, const int32_t* q_lens, int batch, int max_q,
-                                            int nsplit, int workers, int min_tiles, int b) {
-  const RequestScan r = scan_requests(seq_lens, q_lens, batch, max_q);
-  const int C = range_chunk(r, nsplit, workers, min_tiles);
-  const int J = __builtin_amdgcn_readlane(r.J, b);
-  const int tiles = __builtin_amdgcn_readlane(r.tiles, b);
-  return tiles > 0 ? (J + tiles - 1) / C - J / C + 1 : 0;
-}
-
 // Exact recomputation of rows whose fixed-reference row sum reached
 // kRowSumLimit (scores far above the max of the split's first tile): one row at
 // a time across the whole wave, with a running max and a rescale at every key,
@@ -1442,10 +1432,7 @@ __global__ __launch_bounds__(256) void mla_verify_merge_sliced(MergeArgs p) {
   if (b >= p.batch) return;
   const int Q = clamped_q(p.q_lens, p.seq_lens, b, p.max_q_len);
   if (r >= Q * p.heads) return;  // uniform over the workgroup
-  const int ns = p.use_all_splits ? p.nsplit
-                 : p.plan_ranges ? range_pieces(p.seq_lens, p.q_lens, p.batch, p.max_q_len, p.nsplit, p.workers,
-                                                p.min_tiles, b)
-                                 : split_count(p.seq_lens[b], p.nsplit, p.min_tiles);
+  const int ns = p.use_all_splits ? p.nsplit : split_count(p.seq_lens[b], p.nsplit, p.min_tiles);
   int64_t qo = 0;
   for (int i = 0; i < b; ++i) qo += clamped_q(p.q_lens, p.seq_lens, i, p.max_q_len);
 

@@ -115,3 +115,29 @@ def test_one_handle_two_batches(api):
     ref_o, ref_l = _oracle(y)
     eo, el = max_errors(out, lse, ref_o, ref_l)
     assert eo <= OUT_TOL and el <= LSE_TOL
+
+
+@pytest.mark.parametrize("lens,qlens", [([40, 0, 300], [0, 0, 0]), ([0, 0], [0, 0])],
+                         ids=["no draft tokens", "no keys"])
+def test_empty_batch_writes_nothing(api, lens, qlens):
+    """A batch with no rows: the plan has no tiles, no workgroup does any work, nothing is written.
+    Called through the C ABI with small non-empty buffers (the binding refuses empty tensors)."""
+    import ctypes
+
+    from speculative_decode_mla_amd import _lib
+    dev = "cuda"
+    H = 64
+    q = torch.zeros((4, H, I.D_QK), dtype=torch.bfloat16, device=dev)
+    pool = torch.zeros((512, I.D_QK), dtype=torch.bfloat16, device=dev)
+    slot_idx = torch.zeros(max(1, sum(lens)), dtype=torch.int32, device=dev)
+    seq_lens = torch.tensor(lens, dtype=torch.int32, device=dev)
+    q_lens = torch.tensor(qlens, dtype=torch.int32, device=dev)
+    out = torch.full((4, H, I.D_V), 7.0, dtype=torch.bfloat16, device=dev)
+    lse = torch.full((4, H), 7.0, dtype=torch.float32, device=dev)
+    h = api.MlaVerify(H, len(lens), 16, 8, 512, I.SM_SCALE)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    st = _lib.load().mla_verify_run(h._h, P(q), P(pool), P(slot_idx), P(seq_lens), P(q_lens), P(out), P(lse), 8,
+                                    ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    torch.cuda.synchronize()
+    assert st == _lib.MLA_OK
+    assert bool((out == 7.0).all()) and bool((lse == 7.0).all())
