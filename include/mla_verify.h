@@ -49,7 +49,7 @@ extern "C" {
 #endif
 
 #define MLA_OK 0
-#define MLA_ERR_INVALID_ARGUMENT (-1) /* null pointer, bad size, misaligned pointer, nsplit out of range */
+#define MLA_ERR_INVALID_ARGUMENT (-1) /* null pointer, bad size, misaligned pointer, nsplit out of range, unknown form */
 #define MLA_ERR_UNSUPPORTED (-2)      /* d_qk != 576 or d_v != 512 */
 #define MLA_ERR_OUT_OF_MEMORY (-3)    /* workspace allocation failed */
 #define MLA_ERR_HIP (-4)              /* a HIP runtime call or a kernel launch failed, or no GPU */
@@ -69,7 +69,20 @@ typedef struct {
   int32_t max_nsplit; /* >= 1: the workspace holds this many partials per row */
   int64_t num_slots;  /* rows in kv_pool (>= 1) */
   float sm_scale;     /* score scale, > 0 (1/sqrt(192) in the reference workloads) */
+  int32_t form;       /* kernel-1 layout: MLA_VERIFY_FORM_AUTO (0), _128ROW (1) or _TWO_STREAM (2) */
 } mla_verify_config;
+
+/* Kernel-1 layouts (the result is the same up to rounding; they differ in speed).
+ * 128ROW: workgroups of 128 (draft token, head) rows, one 32-key tile per step.
+ * TWO_STREAM: workgroups of 64 rows over two key streams (two tiles per step).
+ * AUTO: TWO_STREAM for requests of at most 64 rows, and for calls whose 128-row
+ * workgroups (B * nsplit * ceil(Q_max*H/128)) would occupy at most half of the
+ * CUs; 128ROW otherwise.  Batches of 2..64 requests in the 128-row form spread
+ * their keys over the CUs by the range plan (see mla_verify_run).  Use a fixed
+ * form to compare or test the layouts. */
+#define MLA_VERIFY_FORM_AUTO 0
+#define MLA_VERIFY_FORM_128ROW 1
+#define MLA_VERIFY_FORM_TWO_STREAM 2
 
 /*
  * Validate `cfg`, allocate the split workspace on the current device

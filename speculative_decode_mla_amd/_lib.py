@@ -15,6 +15,10 @@ MLA_ERR_UNSUPPORTED = -2
 MLA_ERR_OUT_OF_MEMORY = -3
 MLA_ERR_HIP = -4
 
+FORM_AUTO = 0        # kernel-1 layouts (include/mla_verify.h)
+FORM_128ROW = 1
+FORM_TWO_STREAM = 2
+
 D_QK = 576
 D_V = 512
 
@@ -33,6 +37,7 @@ class MlaVerifyConfig(ctypes.Structure):
         ("max_nsplit", ctypes.c_int32),
         ("num_slots", ctypes.c_int64),
         ("sm_scale", ctypes.c_float),
+        ("form", ctypes.c_int32),
     ]
 
 

@@ -48,9 +48,10 @@ class MlaVerify:
     """
 
     def __init__(self, num_heads: int, batch: int, max_q_len: int, max_nsplit: int, num_slots: int,
-                 sm_scale: float = DEFAULT_SCALE):
+                 sm_scale: float = DEFAULT_SCALE, form: int = _lib.FORM_AUTO):
         lib = _lib.load()
-        self.cfg = _lib.MlaVerifyConfig(num_heads, D_QK, D_V, batch, max_q_len, max_nsplit, num_slots, sm_scale)
+        self.cfg = _lib.MlaVerifyConfig(num_heads, D_QK, D_V, batch, max_q_len, max_nsplit, num_slots, sm_scale,
+                                        form)
         h = ctypes.c_void_p()
         _lib.check("mla_verify_create", lib.mla_verify_create(ctypes.byref(self.cfg), ctypes.byref(h)))
         self._h = h

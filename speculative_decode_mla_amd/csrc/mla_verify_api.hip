@@ -14,6 +14,8 @@ struct mla_verify_s {
   int32_t row_groups;
   int32_t rows_pad;
   int32_t streams;    // kernel 1 form: 1 (128-row workgroups) or 2 (64-row workgroups, two key streams)
+  int32_t rows;       // max_q_len * H
+  int32_t cus;        // compute units of the device
   int32_t plan_ranges;  // 1: batches of 2..64 requests in the 128-row form use the range plan
   int32_t workers;      // range plan: workers, one workgroup per row group each (CUs / row groups)
   uint16_t* o_part;  // bf16 [B, max_nsplit, rows_pad, 512]
@@ -56,14 +58,22 @@ int mla_verify_create(const mla_verify_config* cfg, mla_verify_handle* out) {
     return MLA_ERR_INVALID_ARGUMENT;
   if (!(cfg->sm_scale > 0.f) || !std::isfinite(cfg->sm_scale)) return MLA_ERR_INVALID_ARGUMENT;
   if (cfg->d_qk != MLA_VERIFY_D_QK || cfg->d_v != MLA_VERIFY_D_V) return MLA_ERR_UNSUPPORTED;
+  if (cfg->form != MLA_VERIFY_FORM_AUTO && cfg->form != MLA_VERIFY_FORM_128ROW &&
+      cfg->form != MLA_VERIFY_FORM_TWO_STREAM)
+    return MLA_ERR_INVALID_ARGUMENT;
   const int64_t rows = (int64_t)cfg->max_q_len * cfg->num_heads;
   // Requests of at most 64 rows (a q_len = 1 decode step with H <= 64) use the two-stream form of
-  // kernel 1, whose workgroups hold 64 rows; larger ones the 128-row form.
-  const int32_t streams = rows <= mlav::kRowsPerGroup2s ? 2 : 1;
+  // kernel 1, whose workgroups hold 64 rows; larger ones the 128-row form (or, per call, the
+  // two-stream form when the 128-row workgroups would leave most CUs idle; see launch_partials).
+  const int32_t streams = cfg->form == MLA_VERIFY_FORM_TWO_STREAM ? 2
+                          : cfg->form == MLA_VERIFY_FORM_128ROW   ? 1
+                          : rows <= mlav::kRowsPerGroup2s        ? 2 : 1;
   const int64_t group = streams == 2 ? mlav::kRowsPerGroup2s : mlav::kRowsPerGroup;
   const int64_t row_groups = (rows + group - 1) / group;
-  const int64_t rows_pad = row_groups * group;
-  const int64_t grid = (int64_t)cfg->batch * cfg->max_nsplit * row_groups;
+  // (rows past 64 are padded to a multiple of 128, which holds the groups of either form)
+  const int64_t rows_pad = rows <= mlav::kRowsPerGroup2s ? row_groups * group
+                                                         : (rows + mlav::kRowsPerGroup - 1) / mlav::kRowsPerGroup * mlav::kRowsPerGroup;
+  const int64_t grid = (int64_t)cfg->batch * cfg->max_nsplit * ((rows + mlav::kRowsPerGroup2s - 1) / mlav::kRowsPerGroup2s);
   if (rows_pad > INT32_MAX / 2 || grid > INT32_MAX || (int64_t)cfg->batch * rows > INT32_MAX)
     return MLA_ERR_INVALID_ARGUMENT;
 
@@ -80,6 +90,8 @@ int mla_verify_create(const mla_verify_config* cfg, mla_verify_handle* out) {
   h->row_groups = (int32_t)row_groups;
   h->rows_pad = (int32_t)rows_pad;
   h->streams = streams;
+  h->rows = (int32_t)rows;
+  h->cus = cus;
   // A batch in the 128-row form is spread over one workgroup per CU (one resident per CU), as
   // `workers` workers of row_groups workgroups each (the range plan of kernel 1).
   h->plan_ranges = streams == 1 && cfg->batch >= 2 && cfg->batch <= mlav::kRangeMaxBatch && row_groups <= cus;
@@ -131,6 +143,15 @@ int launch_partials(mla_verify_handle h, const void* q, const void* kv_pool, con
   pa.rows_pad = h->rows_pad;
   pa.min_tiles = kMinTilesPerSplit;
   pa.streams = h->streams;
+  // A call whose 128-row workgroups would occupy at most half of the CUs (one request with few
+  // splits, e.g. nsplit 16 with 8 row groups) takes the two-stream form instead: 64-row workgroups,
+  // twice as many, over the same splits, so the partials (and the merge) are the same.  (Decided
+  // from the call's shape alone; kernel 1 may still leave splits of short requests empty.)
+  if (c.form == MLA_VERIFY_FORM_AUTO && pa.streams == 1 && !h->plan_ranges &&
+      2 * (int64_t)c.batch * nsplit * h->row_groups <= h->cus) {
+    pa.streams = 2;
+    pa.row_groups = (h->rows + mlav::kRowsPerGroup2s - 1) / mlav::kRowsPerGroup2s;  // rows_pad (a multiple of 128) holds them
+  }
   pa.plan_ranges = h->plan_ranges;
   pa.workers = h->workers;
   pa.scale_log2 = c.sm_scale * 1.4426950408889634f;

@@ -25,8 +25,9 @@ def api():
     return A
 
 
-def _handle(api, x, nsplit, max_q=None):
-    return api.MlaVerify(x.heads, len(x.seq_lens), max_q or int(max(1, x.q_lens.max())), nsplit, x.num_slots, x.scale)
+def _handle(api, x, nsplit, max_q=None, form=0):
+    return api.MlaVerify(x.heads, len(x.seq_lens), max_q or int(max(1, x.q_lens.max())), nsplit, x.num_slots, x.scale,
+                         form=form)
 
 
 def _oracle(x):
@@ -80,13 +81,14 @@ def test_largest_batch(api):
 
 def test_past_the_plan_per_split(api):
     """65 requests take the per-request splits instead; there a request's result does not depend
-    on the rest of the batch, so it equals the request run alone bit for bit."""
+    on the rest of the batch, so it equals the request run alone bit for bit (both calls pinned to
+    the 128-row form: alone, the request's few workgroups would otherwise take the two-stream form)."""
     rng = np.random.default_rng(58)
     lens = _lens(rng, 65, 20, 1500)
     qlens = [int(min(l, 3)) for l in lens]
     x = I.make_custom(rng, lens, qlens, 32, int(sum(lens)) + 500)
     d = DeviceInputs(x)
-    out, lse = d.run(_handle(api, x, 8, max_q=3), 8)
+    out, lse = d.run(_handle(api, x, 8, max_q=3, form=1), 8)
     torch.cuda.synchronize()
     ref_o, ref_l = _oracle(x)
     eo, el = max_errors(out, lse, ref_o, ref_l)
@@ -97,7 +99,7 @@ def test_past_the_plan_per_split(api):
                        slot_idx=x.slot_idx[k0:k0 + lens[b]], seq_lens=x.seq_lens[b:b + 1],
                        q_lens=x.q_lens[b:b + 1], num_slots=x.num_slots, heads=32)
     e = DeviceInputs(y)
-    o1, l1 = e.run(_handle(api, y, 8, max_q=3), 8)
+    o1, l1 = e.run(_handle(api, y, 8, max_q=3, form=1), 8)
     torch.cuda.synchronize()
     assert torch.equal(out[q0:q0 + qlens[b]], o1) and torch.equal(lse[q0:q0 + qlens[b]], l1)
 

@@ -24,18 +24,24 @@ def api():
     return A
 
 
-def _handle(api, x, nsplit, max_q=None):
-    return api.MlaVerify(x.heads, len(x.seq_lens), max_q or int(max(1, x.q_lens.max())), nsplit, x.num_slots, x.scale)
+# Kernel-1 layouts: 1 = 128-row workgroups (range plan for batches of 2..64), 2 = two-stream 64-row
+# workgroups.  Tests that pin one run it under both.
+FORMS = [1, 2]
 
 
-def _check(api, x, nsplit, label=""):
+def _handle(api, x, nsplit, max_q=None, form=0):
+    return api.MlaVerify(x.heads, len(x.seq_lens), max_q or int(max(1, x.q_lens.max())), nsplit, x.num_slots, x.scale,
+                         form=form)
+
+
+def _check(api, x, nsplit, label="", form=0):
     d = DeviceInputs(x)
-    h = _handle(api, x, nsplit)
+    h = _handle(api, x, nsplit, form=form)
     out, lse = d.run(h, nsplit)
     torch.cuda.synchronize()
     ref_o, ref_l = oracle.verify_attention(x.q, x.pool(), x.slot_idx, x.seq_lens, x.q_lens, x.scale)
     eo, el = max_errors(out, lse, ref_o, ref_l)
-    print(f"{label} nsplit={nsplit}: max|out err|={eo:.3e} max|lse err|={el:.3e}", flush=True)
+    print(f"{label} form={form} nsplit={nsplit}: max|out err|={eo:.3e} max|lse err|={el:.3e}", flush=True)
     assert eo <= OUT_TOL and el <= LSE_TOL
     return d, h
 
@@ -55,13 +61,15 @@ CASES = [
     (26, [300], [16], 64, 2),           # 1024 rows: eight row groups
     (27, [4096 + 37], [16], 16, 8),     # ragged last tile
     (28, [64, 128, 192], [16, 16, 16], 4, 32),  # more splits than tiles
+    (29, [900], [5], 40, 4),            # 200 rows: a ragged last row group in either form
 ]
 
 
+@pytest.mark.parametrize("form", FORMS)
 @pytest.mark.parametrize("seed,lens,qlens,heads,nsplit", CASES)
-def test_small_cases(api, seed, lens, qlens, heads, nsplit):
+def test_small_cases(api, seed, lens, qlens, heads, nsplit, form):
     x = I.make_custom(np.random.default_rng(seed), lens, qlens, heads, int(sum(lens)) * 2 + 64)
-    _check(api, x, nsplit, f"case{seed}")
+    _check(api, x, nsplit, f"case{seed}", form)
 
 
 def test_ctx4k_workload(api):
@@ -98,19 +106,21 @@ def test_full_size_sampled_parity(api, workload):
     torch.cuda.empty_cache()
 
 
-def test_single_key_is_exact(api):
+@pytest.mark.parametrize("form", FORMS)
+def test_single_key_is_exact(api, form):
     x = I.make_custom(np.random.default_rng(30), [1], [1], 64, 100)
     d = DeviceInputs(x)
-    out, lse = d.run(_handle(api, x, 1), 1)
+    out, lse = d.run(_handle(api, x, 1, form=form), 1)
     torch.cuda.synchronize()
     v = torch.from_numpy(x.kv_rows[0, :512].view(np.int16).copy()).view(torch.bfloat16)
     assert torch.equal(out.cpu()[0], v.expand(64, 512))
 
 
-def test_split_count_does_not_change_result(api):
+@pytest.mark.parametrize("form", FORMS)
+def test_split_count_does_not_change_result(api, form):
     x = I.make_custom(np.random.default_rng(31), [3000, 900], [16, 9], 32, 10000)
     d = DeviceInputs(x)
-    h = _handle(api, x, 32)
+    h = _handle(api, x, 32, form=form)
     ref_o, ref_l = oracle.verify_attention(x.q, x.pool(), x.slot_idx, x.seq_lens, x.q_lens, x.scale)
     outs = []
     for ns in (1, 2, 5, 32, 7):
@@ -155,25 +165,27 @@ def test_request_alone_equals_request_in_batch(api):
         assert eo <= OUT_TOL and el <= LSE_TOL
 
 
-def test_overflow_fallback_rows(api):
+@pytest.mark.parametrize("form", FORMS)
+def test_overflow_fallback_rows(api, form):
     """A key far above a row's first-block max sends the row through the exact fallback kernel."""
     x = I.make_custom(np.random.default_rng(35), [2000], [4], 8, 4000)
     q0 = oracle.bf16_bits_to_f64(x.q[0, 3])
     # key 1500 aligned with (token 0, head 3): score ~ 1.6*|q|^2/sqrt(192) ~ 70 nats ~ 100 log2 units
     x.kv_rows[1500] = I.f32_to_bf16_bits((1.6 * q0).astype(np.float32))
-    _check(api, x, 2, "overflow")
-    _check(api, x, 1, "overflow")
+    _check(api, x, 2, "overflow", form)
+    _check(api, x, 1, "overflow", form)
 
 
-def test_overflow_to_inf_fallback_rows(api):
+@pytest.mark.parametrize("form", FORMS)
+def test_overflow_to_inf_fallback_rows(api, form):
     """A key so far above the first tile's max that 2^(x - m_ref) overflows fp32:
     without the exact fallback the row would come out inf/NaN."""
     x = I.make_custom(np.random.default_rng(39), [3000], [4], 8, 6000)
     q0 = oracle.bf16_bits_to_f64(x.q[2, 5])
     # key 2900 aligned with (token 2, head 5): score ~ 2.6*|q|^2/sqrt(192) ~ 108 nats ~ 156 log2 units
     x.kv_rows[2900] = I.f32_to_bf16_bits((2.6 * q0).astype(np.float32))
-    _check(api, x, 3, "overflow-inf")
-    _check(api, x, 1, "overflow-inf")
+    _check(api, x, 3, "overflow-inf", form)
+    _check(api, x, 1, "overflow-inf", form)
 
 
 # with 60 rows: 6 splits take the 4-group merge, 80 and 300 the column-sliced one (300: more
