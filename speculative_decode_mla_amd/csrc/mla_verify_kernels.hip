@@ -1014,13 +1014,19 @@ void mla_verify_partial_2s(PartialArgs p) {
     for (int j = 0; j < 4; ++j) kaddr[j] = base + (((2 * j) ^ hi ^ f) << 4);
   }
 
-  // ---- prologue: slot indices of tile 0, the q rows staged through ring buffer w (as in the
-  // 128-row form), then tile 0 ----------------------------------------------------------------
+  // ---- prologue: slot indices of tile 0, the q rows, then tile 0 while the q rows land ----------
+  // The two streams hold the same 64 rows, so the rows are staged once, through ring buffers 2 and 3
+  // (rows of wave half h in buffer 2 + h, in the key-tile layout as in the 128-row form), and tile 0
+  // of each stream (buffers 0 and 1) is gathered while they arrive.  Both waves of a half issue the
+  // same q loads (the same bytes to the same place), which keeps the code free of branches between
+  // the untracked slot loads and their wait.  Tile 1 goes to buffers 2 and 3 in the first step,
+  // after the barrier that follows every wave's q reads.
   int sl[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) sl[j] = load_b32_untracked(slots_g + gather_key(0, j));
+  static_assert(4 * kDmaPerTile == 36 && 2 * kDmaPerTile == 18, "wait counts below");
   {
-    const uint32_t qbuf = smem_base + w_uniform * kTileBytes;
+    const uint32_t qbuf = smem_base + (2 + (w_uniform & 1)) * kTileBytes;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       const int r = row0 + half * kRowsPerWave + 8 * kb + g_kr;
@@ -1028,20 +1034,24 @@ void mla_verify_partial_2s(PartialArgs p) {
       dma_key_block((const char*)(p.q + qrow * kDqk) + (((lane & 7) ^ g_kr ^ (kb & 1)) << 4), qbuf + kb * kKeyBlockBytes);
     }
   }
-  asm volatile("s_waitcnt vmcnt(0)" : "+v"(sl[0]), "+v"(sl[1]) : : "memory");
+  // the slot indices have landed (the 36 q loads issued after them may still be in flight)
+  asm volatile("s_waitcnt vmcnt(36)" : "+v"(sl[0]), "+v"(sl[1]) : : "memory");
+  if (nst > 0) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) dma_key_block(g_row(sl[j], j), g_lds(0, j));
+    MLAV_WAIT_VMCNT(18);  // the q rows have landed (tile 0's 18 loads may still be in flight)
+  } else {
+    MLAV_WAIT_VMCNT(0);
+  }
+  __syncthreads();  // every wave's q rows are visible
   bf16x8 qf[kQkSteps];
   {
-    const lds_char* qb = smem + w * kTileBytes;
+    const lds_char* qb = smem + (2 + (w_uniform & 1)) * kTileBytes;
 #pragma unroll
     for (int ks = 0; ks < kQkSteps; ++ks)
       qf[ks] = *(const __attribute__((address_space(3))) bf16x8*)(qb + kaddr[ks & 3] + (ks >> 2) * kBlockBytes);
   }
-  asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
-  __syncthreads();
-  if (nst > 0) {
-#pragma unroll
-    for (int j = 0; j < 2; ++j) dma_key_block(g_row(sl[j], j), g_lds(0, j));
-  }
+  asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");  // (the first step's barrier then frees buffers 2, 3)
   int sn[2];  // slots of the next tile to gather (compiler-tracked loads, awaited at the next step)
 #pragma unroll
   for (int j = 0; j < 2; ++j) sn[j] = slots_g[gather_key(1, j)];
