@@ -948,6 +948,7 @@ constexpr int kMergeUnroll = 8;
 constexpr int kMergeGroupsFew = 16;
 constexpr int kMergeFewRows = 512;      // fewer rows per call than this ...
 constexpr int kMergeManySplits = 64;    // ... and at least this many splits: the forms for few rows
+constexpr int kMergeWaveSplits = 32;    // up to this many splits: one wave per row
 
 // Eight consecutive partial values: loaded raw (so that a batch of loads is in flight at
 // once), widened to fp32 when used.
@@ -1542,15 +1543,18 @@ hipError_t launch_partial(const PartialArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream) {
-  if (a.plan_ranges) {  // (bf16 partials of the library's workspace)
+  const int64_t rows = (int64_t)a.batch * a.max_q_len * a.heads;  // one workgroup per row below
+  const bool few = rows < kMergeFewRows && a.nsplit >= kMergeManySplits;
+  // The library's bf16 partials with at most kMergeWaveSplits per row (the range plan, or a call such
+  // as ctx64k's 32 splits): one wave per row, four rows per workgroup.  At ctx64k this took 0.7 us
+  // less per call than 256 threads per row, measured on one box.
+  if (a.plan_ranges || (!a.part_fp32 && !few && a.nsplit <= kMergeWaveSplits)) {
     constexpr int kRowsPerBlock = 4;
     const int64_t blocks = (int64_t)a.batch * ((a.max_q_len * a.heads + kRowsPerBlock - 1) / kRowsPerBlock);
     hipLaunchKernelGGL((mla_verify_merge_kernel<__bf16, 1, kRowsPerBlock>), dim3((unsigned)blocks),
                        dim3(64 * kRowsPerBlock), 0, stream, a);
     return hipGetLastError();
   }
-  const int64_t rows = (int64_t)a.batch * a.max_q_len * a.heads;  // one workgroup per row
-  const bool few = rows < kMergeFewRows && a.nsplit >= kMergeManySplits;
   if (few && a.nsplit <= kSliceMaxSplits) {
     const dim3 grid((unsigned)(rows * (kDv / kSliceCols)));
     if (a.part_fp32)

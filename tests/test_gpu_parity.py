@@ -62,6 +62,8 @@ CASES = [
     (27, [4096 + 37], [16], 16, 8),     # ragged last tile
     (28, [64, 128, 192], [16, 16, 16], 4, 32),  # more splits than tiles
     (29, [900], [5], 40, 4),            # 200 rows: a ragged last row group in either form
+    (41, [2000], [16], 128, 8),         # 128 heads: 2,048 rows, 16 (or 32) row groups
+    (42, [900, 1300], [16, 8], 128, 4),  # 128 heads in the range plan: 16 workers of 16 row groups
 ]
 
 
