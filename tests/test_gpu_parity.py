@@ -231,21 +231,27 @@ def test_stale_workspace_is_not_read(api):
     assert eo <= OUT_TOL and el <= LSE_TOL
 
 
-def test_graph_replay_matches_eager(api):
-    x = I.make_custom(np.random.default_rng(39), [3000, 1000], [16, 16], 16, 8000)
+@pytest.mark.parametrize("seed,lens,qlens,heads,nsplit", [
+    (39, [3000, 1000], [16, 16], 16, 8),   # two requests: the range plan
+    (43, [5000], [16], 64, 16),            # one request, 16 x 8 row groups: the two-stream form (automatic)
+    (44, [9000], [16], 64, 32),            # one request, 32 x 8 row groups: the 128-row form
+    (45, [4000, 700], [1, 1], 64, 32),     # a decode step: 64 rows per request, the two-stream form
+], ids=["range plan", "two-stream", "128-row", "decode"])
+def test_graph_replay_matches_eager(api, seed, lens, qlens, heads, nsplit):
+    x = I.make_custom(np.random.default_rng(seed), lens, qlens, heads, int(sum(lens)) * 2 + 64)
     d = DeviceInputs(x)
-    h = _handle(api, x, 8)
-    out_e, lse_e = (t.clone() for t in d.run(h, 8))
+    h = _handle(api, x, nsplit)
+    out_e, lse_e = (t.clone() for t in d.run(h, nsplit))
     torch.cuda.synchronize()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
-        d.run(h, 8)  # warm-up on the capture stream
+        d.run(h, nsplit)  # warm-up on the capture stream
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        d.run(h, 8)
+        d.run(h, nsplit)
     for i in range(4):
         d.out.fill_(0)
         d.lse.fill_(0)
@@ -253,7 +259,7 @@ def test_graph_replay_matches_eager(api):
         torch.cuda.synchronize()
         assert torch.equal(d.out, out_e) and torch.equal(d.lse, lse_e), f"replay {i}"
         # eager work between replays
-        d.run(h, 8)
+        d.run(h, nsplit)
         torch.cuda.synchronize()
 
 
