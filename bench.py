@@ -263,6 +263,7 @@ def main():
     ap.add_argument("--workload", default="ctx64k")
     ap.add_argument("--nsplit", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold", type=int, default=50, help="single-call replays, each after reading 1 GiB to flush the caches")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for the CPU baseline")
     ap.add_argument("--eager", action="store_true", help="plain launches, no graph (for profilers)")
     ap.add_argument("--copy-calib", action="store_true",
@@ -350,6 +351,7 @@ def main():
         us = wall / args.steps * 1e6
         times_us = [us]
         steady_us = [us]
+        cold_us = []
         k1_us = float("nan")
     else:
         side = torch.cuda.Stream()
@@ -405,6 +407,22 @@ def main():
             b.record(stream)
         torch.cuda.synchronize()
         k1_us = statistics.median(a.elapsed_time(b) * 1e3 / 10 for a, b in kev)
+        # (last: the flushes disturb the timings that follow them)
+        # cold single calls: 1 GiB read before each replay (outside the events) evicts the KV rows from
+        # the L2s and the 256 MB MALL, so the call reads them from HBM.  A read, not a write: written
+        # lines would still be dirty in the caches and their write-back would land inside the call.
+        flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        flush.sum()
+        torch.cuda.synchronize()
+        cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.cold)]
+        for a, b in cev:
+            flush.sum()
+            a.record(stream)
+            g.replay()
+            b.record(stream)
+        torch.cuda.synchronize()
+        cold_us = sorted(a.elapsed_time(b) * 1e3 for a, b in cev)
+        del flush
         us = sum(steady_us) / len(steady_us)
 
     flops, kv_bytes, alg_bytes = algorithmic_counts(x)
@@ -452,6 +470,8 @@ def main():
         "steady_p50_us": round(statistics.median(steady_us), 3),
         "single_call_p50_us": round(statistics.median(times_us), 3),
         "single_call_p95_us": round(p95, 3),
+        "cold_single_call_p50_us": round(statistics.median(cold_us), 3) if cold_us else None,
+        "cold_kv_gbps": round(kv_bytes / (statistics.median(cold_us) * 1e-6) / 1e9, 1) if cold_us else None,
         "wall_us_per_step": round(wall / args.steps * 1e6, 3),
         "kv_gbps": round(kv_bytes / (us * 1e-6) / 1e9, 1),
         "kv_frac_of_hbm": round(kv_bytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
