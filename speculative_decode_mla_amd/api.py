@@ -45,6 +45,8 @@ class MlaVerify:
 
     run() enqueues the two kernels on the current (or given) stream and returns
     without synchronising, so it can be captured in a torch.cuda.CUDAGraph.
+    `form` picks kernel 1's layout (FORM_AUTO, FORM_128ROW or FORM_TWO_STREAM from
+    _lib); the result is the same up to rounding, only the speed differs.
     """
 
     def __init__(self, num_heads: int, batch: int, max_q_len: int, max_nsplit: int, num_slots: int,
