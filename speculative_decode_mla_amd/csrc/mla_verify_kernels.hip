@@ -394,14 +394,15 @@ __device__ __forceinline__ bool decode_piece(const PartialArgs& p, int wg, WorkI
   const int x = pools == 8 ? (wg & 7) : 0, kk = pools == 8 ? (wg >> 3) : wg;
   int j = kk / p.row_groups;
   const int g = kk - j * p.row_groups;
-  // pieces of each of the pool's workers (worker x + pools*i in lane i)
+  // pieces of each of the pool's workers (worker x + pools*i in lane i; at most 64 workers per pool,
+  // which the worker count chosen at create guarantees)
   int npieces = 0;
   for (int i = 0; i < per_pool; ++i) {
     const int o = x + pools * i;
     if ((int64_t)o * C >= T) break;
     const int lo = o * C, hi = lo + (C < T - lo ? C : T - lo);
     const int n = __popcll(chunk_requests(r, lo, hi));
-    if (lane == (i & 63) && i < 64) npieces = n;
+    if (lane == i) npieces = n;
   }
   // round k holds the k-th largest piece of each chunk with more than k pieces, workers in order
   int o = -1, k = 0;
