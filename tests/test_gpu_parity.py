@@ -64,6 +64,8 @@ CASES = [
     (29, [900], [5], 40, 4),            # 200 rows: a ragged last row group in either form
     (41, [2000], [16], 128, 8),         # 128 heads: 2,048 rows, 16 (or 32) row groups
     (42, [900, 1300], [16, 8], 128, 4),  # 128 heads in the range plan: 16 workers of 16 row groups
+    (46, [16], [16], 64, 2),            # every key is a draft key: draft t sees keys 0..t only
+    (47, [40, 16, 3], [16, 16, 3], 16, 4),  # the same inside a batch, next to a longer request
 ]
 
 
@@ -106,6 +108,41 @@ def test_full_size_sampled_parity(api, workload):
     assert eo <= OUT_TOL and el <= LSE_TOL
     del d, h
     torch.cuda.empty_cache()
+
+
+def test_long_context_sampled_parity(api):
+    """262,144 keys (past the largest workload) at nsplit 64, sampled rows against the oracle."""
+    x = I.make_custom(np.random.default_rng(48), [1 << 18], [16], 64, 1 << 19)
+    d = DeviceInputs(x)
+    h = _handle(api, x, 64)
+    out, lse = d.run(h, 64)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(98)
+    rows = [(0, 0), (15, 63)] + [(int(t), int(hh)) for t, hh in zip(rng.integers(0, 16, 6), rng.integers(0, 64, 6))]
+    ref_o, ref_l = oracle.verify_attention_rows(x.q, x.sparse_pool(), x.slot_idx, x.seq_lens, x.q_lens, x.scale, rows)
+    o = bf16_to_f64(out)
+    l = lse.cpu().numpy().astype(np.float64)
+    eo = max(float(np.max(np.abs(o[t, hh] - ref_o[i]))) for i, (t, hh) in enumerate(rows))
+    el = max(abs(float(l[t, hh]) - ref_l[i]) for i, (t, hh) in enumerate(rows))
+    print(f"ctx256k nsplit=64: max|out err|={eo:.3e} max|lse err|={el:.3e}", flush=True)
+    assert eo <= OUT_TOL and el <= LSE_TOL
+    del d, h
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("form", FORMS)
+def test_pool_edge_slots(api, form):
+    """Slot indices at the first and the last row of the pool (the gather's address range ends)."""
+    x = I.make_custom(np.random.default_rng(49), [700, 300], [8, 8], 16, 2000)
+    s = x.slot_idx.copy()
+    for want, pos in ((0, 5), (x.num_slots - 1, len(s) - 1)):  # swap so the slots stay distinct
+        j = np.nonzero(s == want)[0]
+        if len(j):
+            s[j[0]] = s[pos]
+        s[pos] = want
+    y = I.VerifyInputs(q=x.q, kv_rows=x.kv_rows, slot_idx=s, seq_lens=x.seq_lens, q_lens=x.q_lens,
+                       num_slots=x.num_slots, heads=x.heads)
+    _check(api, y, 4, "pool-edge", form)
 
 
 @pytest.mark.parametrize("form", FORMS)
