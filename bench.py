@@ -260,6 +260,8 @@ def main():
     # fresh process ran ~5 % slower than the same graphs 0.1 s later.  1,000 untimed calls (0.13 s at
     # ctx64k) cover that.
     ap.add_argument("--warmup", type=int, default=1000)
+    ap.add_argument("--settle", type=float, default=0.5,
+                    help="seconds of untimed back-to-back calls before the timed region (besides --warmup)")
     ap.add_argument("--workload", default="ctx64k")
     ap.add_argument("--nsplit", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -339,6 +341,7 @@ def main():
           file=sys.stderr, flush=True)
 
     stream = torch.cuda.current_stream()
+    settle_s, settle_calls = 0.0, 0
     if args.eager:
         for _ in range(args.warmup):
             step()
@@ -377,6 +380,17 @@ def main():
         for _ in range(args.warmup):
             g.replay()
         torch.cuda.synchronize()
+        # Untimed settle, whatever --warmup is: the GPU needs about 0.1 s of sustained work before
+        # its clocks (and so the timings) are steady, and a handful of warm-up calls is far less.
+        # Replays of the 10-call graph until args.settle seconds have passed.
+        t_settle = time.perf_counter()
+        settle_calls = 0
+        while time.perf_counter() - t_settle < args.settle:
+            for _ in range(10):
+                gs.replay()
+            settle_calls += 10 * reps
+            torch.cuda.synchronize()
+        settle_s = time.perf_counter() - t_settle
         # the timed region: exactly `steps` calls
         n_rep = args.steps // reps
         sev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_rep)]
@@ -398,10 +412,13 @@ def main():
         torch.cuda.synchronize()
         times_us = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
         # kernel 1 alone: `reps` back-to-back launches per replay, timed with events on the same stream
+        # (interleaved with replays of the call graph, so that the GPU stays as busy as in the timed
+        # region); then the merge's share of a call as the difference
         gk.replay()
         torch.cuda.synchronize()
-        kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
+        kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(40)]
         for a, b in kev:
+            gs.replay()
             a.record(stream)
             gk.replay()
             b.record(stream)
@@ -437,19 +454,26 @@ def main():
     two_stream = req_rows <= 64 or (not range_plan and 2 * w.batch * nsplit * -(-req_rows // 128)
                                     <= torch.cuda.get_device_properties(0).multi_processor_count)
     k1_kernel = "mla_verify_partial_2s" if two_stream else "mla_verify_partial"
+    # `achieved`/`frac` are the dominant kernel's (kernel 1: all of the call's FLOPs, and its KV
+    # stream); `call_achieved`/`call_frac` hold the whole captured call (kernel 1, the merge and the
+    # gap between them) against the same roof.
     if flops / alg_bytes >= ridge:
+        call_tflops = flops / (us * 1e-6) / 1e12
         roofline = {"bound": "mfma", "kernel": k1_kernel,
                     "achieved": round(k1_tflops, 1) if k1_tflops else None, "peak": PEAK_BF16_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(k1_tflops / PEAK_BF16_TFLOPS, 4) if k1_tflops else None,
                     "traffic": measured_traffic(w.name), "traffic_unit": "bytes/launch",
-                    "flops_per_launch": flops}
+                    "flops_per_launch": flops,
+                    "call_achieved": round(call_tflops, 1), "call_frac": round(call_tflops / PEAK_BF16_TFLOPS, 4)}
     else:
         k1_gbps = alg_bytes / (k1_us * 1e-6) / 1e9 if k1_us == k1_us else None
+        call_gbps = alg_bytes / (us * 1e-6) / 1e9
         roofline = {"bound": "hbm", "kernel": k1_kernel,
                     "achieved": round(k1_gbps, 1) if k1_gbps else None, "peak": PEAK_HBM_GBPS,
                     "unit": "GB/s", "frac": round(k1_gbps / PEAK_HBM_GBPS, 4) if k1_gbps else None,
                     "traffic": measured_traffic(w.name), "traffic_unit": "bytes/launch",
-                    "bytes_per_launch": alg_bytes}
+                    "bytes_per_launch": alg_bytes,
+                    "call_achieved": round(call_gbps, 1), "call_frac": round(call_gbps / PEAK_HBM_GBPS, 4)}
     res = {
         "metric": METRIC,
         "value": round(us, 3),
@@ -467,6 +491,8 @@ def main():
                    "context": w.ctx if w.ctx else "log-uniform[1024,65536] (seed 5)",
                    "pool_slots": w.num_slots, "nsplit": nsplit, "replay": "eager" if args.eager else "hipGraph, 10 calls per graph",
                    "seed": w.seed},
+        "settle_s": round(settle_s, 3),
+        "settle_calls": settle_calls,
         "steady_p50_us": round(statistics.median(steady_us), 3),
         "single_call_p50_us": round(statistics.median(times_us), 3),
         "single_call_p95_us": round(p95, 3),

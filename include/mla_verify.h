@@ -206,6 +206,22 @@ int mla_verify_build_metadata(const int32_t* req_to_token, int32_t table_rows, i
                               const int32_t* draft_lens, int32_t batch, int32_t* slot_idx, int64_t slot_capacity,
                               int32_t* seq_lens, int32_t* q_lens, int32_t* status, void* stream);
 
+/*
+ * Where a handle's split workspace lives (the partials kernel 1 writes and the
+ * merge reads in mla_verify_run), for inspection and tests:
+ *   *o_part   device bf16 [batch, max_nsplit, rows_pad, 512], rows_pad =
+ *             ceil(max_q_len * H / 128) * 128 (row r of request b is (token r / H,
+ *             head r % H)); *o_part_bytes its size.
+ *   *lse_part device fp32 [batch, max_nsplit, rows_pad]; *lse_part_bytes its size.
+ * The library owns the memory (freed by mla_verify_destroy).  Every call
+ * overwrites the partials it reads before reading them; what the workspace
+ * holds between calls has no meaning, and writing into it between calls (for
+ * instance filling it with NaN) does not change any later call's result.
+ * Any output pointer may be NULL.  Errors: INVALID_ARGUMENT (null handle).
+ */
+int mla_verify_workspace(mla_verify_handle h, void** o_part, int64_t* o_part_bytes, void** lse_part,
+                         int64_t* lse_part_bytes);
+
 /* Free the workspace and the handle.  NULL is a no-op.  The caller must make
  * sure no enqueued call still uses the handle (synchronise its stream first). */
 int mla_verify_destroy(mla_verify_handle h);

@@ -206,5 +206,5 @@ def verify_attention_split(q, kv_pool, slot_idx, seq_lens, q_lens, scale, nsplit
 
 __all__ = [
     "bf16_bits_to_f64", "visible_count", "verify_attention", "verify_attention_rows",
-    "verify_attention_split", "merge_partials", "split_bounds", "math",
+    "verify_attention_split", "merge_partials", "split_bounds",
 ]

@@ -49,6 +49,8 @@ SIGNATURES = {
     "mla_verify_compact": (ctypes.c_int, [_P, _P, ctypes.c_int64, _P, ctypes.c_int64, ctypes.c_int64, _P, _P]),
     "mla_verify_build_metadata": (ctypes.c_int, [_P, _I32, _I32, ctypes.c_int64, _P, _P, _P, _I32, _P,
                                                   ctypes.c_int64, _P, _P, _P, _P]),
+    "mla_verify_workspace": (ctypes.c_int, [_P, ctypes.POINTER(_P), ctypes.POINTER(ctypes.c_int64),
+                                            ctypes.POINTER(_P), ctypes.POINTER(ctypes.c_int64)]),
     "mla_verify_destroy": (ctypes.c_int, [_P]),
     "mla_verify_error_string": (ctypes.c_char_p, [ctypes.c_int]),
 }

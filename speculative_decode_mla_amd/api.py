@@ -71,6 +71,15 @@ class MlaVerify:
         except Exception:
             pass
 
+    def workspace(self):
+        """(o_part pointer, its bytes, lse_part pointer, its bytes) of the handle's split workspace
+        (device memory the library owns; see mla_verify_workspace)."""
+        op, lp = ctypes.c_void_p(), ctypes.c_void_p()
+        ob, lb = ctypes.c_int64(), ctypes.c_int64()
+        _lib.check("mla_verify_workspace", _lib.load().mla_verify_workspace(
+            self._h, ctypes.byref(op), ctypes.byref(ob), ctypes.byref(lp), ctypes.byref(lb)))
+        return op.value, ob.value, lp.value, lb.value
+
     def _check_inputs(self, q, kv_pool, slot_idx, seq_lens, q_lens):
         H = self.num_heads
         _need(q, "q", torch.bfloat16, 3)

@@ -279,6 +279,17 @@ int mla_verify_build_metadata(const int32_t* req_to_token, int32_t table_rows, i
   return mlav::launch_step_metadata(a, static_cast<hipStream_t>(stream)) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
+int mla_verify_workspace(mla_verify_handle h, void** o_part, int64_t* o_part_bytes, void** lse_part,
+                         int64_t* lse_part_bytes) {
+  if (h == nullptr) return MLA_ERR_INVALID_ARGUMENT;
+  const int64_t rows = (int64_t)h->cfg.batch * h->cfg.max_nsplit * h->rows_pad;
+  if (o_part != nullptr) *o_part = h->o_part;
+  if (o_part_bytes != nullptr) *o_part_bytes = rows * mlav::kDv * (int64_t)sizeof(uint16_t);
+  if (lse_part != nullptr) *lse_part = h->lse_part;
+  if (lse_part_bytes != nullptr) *lse_part_bytes = rows * (int64_t)sizeof(float);
+  return MLA_OK;
+}
+
 int mla_verify_destroy(mla_verify_handle h) {
   if (h == nullptr) return MLA_OK;
   int st = MLA_OK;

@@ -46,3 +46,28 @@ def max_errors(out_gpu: torch.Tensor, lse_gpu: torch.Tensor, out_ref: np.ndarray
     finite = np.isfinite(lse_ref)
     assert np.array_equal(np.isfinite(l), finite), "-inf pattern of lse differs"
     return float(np.max(np.abs(o - out_ref))), float(np.max(np.abs(l[finite] - lse_ref[finite]), initial=0.0))
+
+
+class _DeviceArray:
+    """A raw device allocation seen through __cuda_array_interface__ (torch wraps it without a copy)."""
+
+    def __init__(self, ptr: int, nbytes: int, typestr: str, itemsize: int):
+        self.__cuda_array_interface__ = {"shape": (nbytes // itemsize,), "typestr": typestr,
+                                         "data": (ptr, False), "version": 2, "strides": None}
+
+
+def workspace_tensors(handle):
+    """The handle's split workspace as torch tensors sharing its memory: (o_part int16, lse_part fp32)."""
+    op, ob, lp, lb = handle.workspace()
+    o = torch.as_tensor(_DeviceArray(op, ob, "<i2", 2), device="cuda")
+    l = torch.as_tensor(_DeviceArray(lp, lb, "<f4", 4), device="cuda")
+    assert o.data_ptr() == op and l.data_ptr() == lp
+    return o, l
+
+
+def poison_workspace(handle):
+    """Fill the workspace with NaN: bf16 0x7FC0 in every partial, fp32 NaN in every LSE."""
+    o, l = workspace_tensors(handle)
+    o.fill_(I.BF16_QNAN)
+    l.fill_(float("nan"))
+    torch.cuda.synchronize()

@@ -27,7 +27,7 @@ def lib():
 def test_header_declares_the_boundary():
     assert _declared() == ["mla_verify_build_metadata", "mla_verify_compact", "mla_verify_create",
                            "mla_verify_destroy", "mla_verify_error_string", "mla_verify_merge",
-                           "mla_verify_partials", "mla_verify_run"]
+                           "mla_verify_partials", "mla_verify_run", "mla_verify_workspace"]
 
 
 def test_every_declared_symbol_is_exported(lib):

@@ -11,7 +11,7 @@ import torch
 
 import oracle
 from speculative_decode_mla_amd import inputs as I
-from tests.gpu_helpers import LSE_TOL, OUT_TOL, DeviceInputs, bf16_to_f64, bits_to_bf16, max_errors
+from tests.gpu_helpers import LSE_TOL, OUT_TOL, DeviceInputs, bf16_to_f64, max_errors, poison_workspace
 
 pytestmark = pytest.mark.gpu
 
@@ -80,54 +80,32 @@ def test_ctx4k_workload(api):
     _check(api, I.make_inputs("ctx4k"), 8, "ctx4k")
 
 
+def _check_full(api, x, nsplit, label):
+    """Whole out and lse tensors against the oracle, element by element (the oracle reads the pool
+    through a sparse view, so the unreferenced rows of a multi-GB pool are never materialised)."""
+    print(f"{label}: B={len(x.seq_lens)} H={x.heads} sum(L)={int(x.seq_lens.sum())} nsplit={nsplit}", flush=True)
+    d = DeviceInputs(x)
+    h = _handle(api, x, nsplit)
+    out, lse = d.run(h, nsplit)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle.verify_attention(x.q, x.sparse_pool(), x.slot_idx, x.seq_lens, x.q_lens, x.scale)
+    eo, el = max_errors(out, lse, ref_o, ref_l)
+    print(f"{label}: {ref_o.shape[0] * ref_o.shape[1]} rows, max|out err|={eo:.3e} max|lse err|={el:.3e}", flush=True)
+    assert eo <= OUT_TOL and el <= LSE_TOL
+    del d, h
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("workload", ["ctx23k", "ctx64k", "ctx91k", "batch16"])
-def test_full_size_sampled_parity(api, workload):
-    """The large workloads at their full sizes and split counts (as the benchmark runs them),
-    checked at sampled (token, head) outputs, which the oracle evaluates one by one: every
-    request's first and last draft token, first and last head, plus seeded random rows."""
-    w = I.WORKLOADS[workload]
-    x = I.make_inputs(workload)
-    d = DeviceInputs(x)
-    h = _handle(api, x, w.nsplit)
-    out, lse = d.run(h, w.nsplit)
-    torch.cuda.synchronize()
-    qo = np.concatenate([[0], np.cumsum(x.q_lens)])
-    rows = []
-    for b in range(len(x.q_lens)):
-        for t in (int(qo[b]), int(qo[b + 1]) - 1):
-            rows += [(t, 0), (t, x.heads - 1)]
-    rng = np.random.default_rng(99)
-    rows += [(int(t), int(hh)) for t, hh in zip(rng.integers(0, x.q.shape[0], 16), rng.integers(0, x.heads, 16))]
-    ref_o, ref_l = oracle.verify_attention_rows(x.q, x.sparse_pool(), x.slot_idx, x.seq_lens, x.q_lens, x.scale, rows)
-    o = bf16_to_f64(out)
-    l = lse.cpu().numpy().astype(np.float64)
-    eo = max(float(np.max(np.abs(o[t, hh] - ref_o[i]))) for i, (t, hh) in enumerate(rows))
-    el = max(abs(float(l[t, hh]) - ref_l[i]) for i, (t, hh) in enumerate(rows))
-    print(f"{workload} nsplit={w.nsplit}, {len(rows)} sampled rows: max|out err|={eo:.3e} max|lse err|={el:.3e}",
-          flush=True)
-    assert eo <= OUT_TOL and el <= LSE_TOL
-    del d, h
-    torch.cuda.empty_cache()
+def test_full_size_parity(api, workload):
+    """The large workloads at their full sizes and split counts, as the benchmark runs them: every
+    (token, head) row of out and lse against the oracle."""
+    _check_full(api, I.make_inputs(workload), I.WORKLOADS[workload].nsplit, workload)
 
 
-def test_long_context_sampled_parity(api):
-    """262,144 keys (past the largest workload) at nsplit 64, sampled rows against the oracle."""
-    x = I.make_custom(np.random.default_rng(48), [1 << 18], [16], 64, 1 << 19)
-    d = DeviceInputs(x)
-    h = _handle(api, x, 64)
-    out, lse = d.run(h, 64)
-    torch.cuda.synchronize()
-    rng = np.random.default_rng(98)
-    rows = [(0, 0), (15, 63)] + [(int(t), int(hh)) for t, hh in zip(rng.integers(0, 16, 6), rng.integers(0, 64, 6))]
-    ref_o, ref_l = oracle.verify_attention_rows(x.q, x.sparse_pool(), x.slot_idx, x.seq_lens, x.q_lens, x.scale, rows)
-    o = bf16_to_f64(out)
-    l = lse.cpu().numpy().astype(np.float64)
-    eo = max(float(np.max(np.abs(o[t, hh] - ref_o[i]))) for i, (t, hh) in enumerate(rows))
-    el = max(abs(float(l[t, hh]) - ref_l[i]) for i, (t, hh) in enumerate(rows))
-    print(f"ctx256k nsplit=64: max|out err|={eo:.3e} max|lse err|={el:.3e}", flush=True)
-    assert eo <= OUT_TOL and el <= LSE_TOL
-    del d, h
-    torch.cuda.empty_cache()
+def test_long_context_parity(api):
+    """262,144 keys (past the largest workload) at nsplit 64, whole tensors against the oracle."""
+    _check_full(api, I.make_custom(np.random.default_rng(48), [1 << 18], [16], 64, 1 << 19), 64, "ctx256k")
 
 
 @pytest.mark.parametrize("form", FORMS)
@@ -251,6 +229,31 @@ def test_merge_kernel_alone(api, S):
     api.merge(torch.from_numpy(op).to(dev), torch.from_numpy(lp).to(dev), torch.from_numpy(x.q_lens).to(dev), out, lse)
     torch.cuda.synchronize()
     eo, el = max_errors(out, lse, ref_o, ref_l)
+    assert eo <= OUT_TOL and el <= LSE_TOL
+
+
+@pytest.mark.parametrize("seed,lens,qlens,heads,nsplit,form", [
+    (60, [9000], [16], 64, 32, 0),               # one request, 32 x 8 row groups: 128-row form
+    (61, [5000], [16], 64, 16, 0),               # one request, 16 x 8 row groups: two-stream form (automatic)
+    (62, [3000, 1000, 37], [16, 16, 5], 16, 8, 0),  # three requests: the range plan
+    (63, [4000, 700], [1, 1], 64, 32, 0),        # a decode step: 64 rows per request, two-stream form
+    (64, [2500, 90, 1], [9, 3, 1], 24, 6, 1),    # ragged, forced 128-row form
+    (65, [2500, 90, 1], [9, 3, 1], 24, 6, 2),    # ragged, forced two-stream form
+    (66, [3000], [4], 8, 64, 0),                 # more splits asked for than the request fills
+], ids=["128-row", "two-stream", "range plan", "decode", "ragged 128-row", "ragged two-stream", "unused splits"])
+def test_nan_workspace_is_not_read(api, seed, lens, qlens, heads, nsplit, form):
+    """The split workspace filled with NaN before the call: every partial the merge reads must have
+    been written by the same call, so out and lse come out finite and match the oracle."""
+    x = I.make_custom(np.random.default_rng(seed), lens, qlens, heads, int(sum(lens)) * 2 + 64)
+    d = DeviceInputs(x)
+    h = _handle(api, x, nsplit, form=form)
+    poison_workspace(h)
+    out, lse = d.run(h, nsplit)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out.float()).all()) and bool(torch.isfinite(lse).all())
+    ref_o, ref_l = oracle.verify_attention(x.q, x.pool(), x.slot_idx, x.seq_lens, x.q_lens, x.scale)
+    eo, el = max_errors(out, lse, ref_o, ref_l)
+    print(f"NaN workspace case {seed}: max|out err|={eo:.3e} max|lse err|={el:.3e}", flush=True)
     assert eo <= OUT_TOL and el <= LSE_TOL
 
 

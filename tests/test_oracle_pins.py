@@ -246,6 +246,7 @@ def _pins_pass():
         lambda: test_p1_matches_torch_sdpa(2, [33, 8], [3, 8], 4),
         test_p2_single_token_returns_v_row,
         test_p3_zero_query_gives_prefix_means,
+        lambda: test_p5_split_equals_unsplit(3),
         test_p6_first_masked_key_does_not_move_output,
         test_p8_two_key_closed_form,
     ]
@@ -257,7 +258,20 @@ def _pins_pass():
     return True
 
 
+_ORIG_ATTEND = om._attend
+_ORIG_MERGE = om.merge_partials
+
+
+def _gather_transposed(kv_pool, slot_idx, start, count):
+    # the gathered [count, 576] block read back as if it were stored [576, count]
+    rows = om.bf16_bits_to_f64(kv_pool[np.asarray(slot_idx[start:start + count], dtype=np.int64)])
+    return rows.reshape(om.D_QK, count).T.copy()
+
+
 MUTANTS = {
+    "transposed key operand (rows read as columns)": ("_gather_keys", _gather_transposed),
+    "base-2 LSE": ("_attend", lambda q, k, scale: (lambda o, l: (o, l / math.log(2.0)))(*_ORIG_ATTEND(q, k, scale))),
+    "last split dropped in the merge": ("merge_partials", lambda o, l: _ORIG_MERGE(o[:-1], l[:-1])),
     "mask off by one (drop own row)": ("visible_count", lambda L, Q, t: L - Q + t),
     "mask off by one (see next draft)": ("visible_count", lambda L, Q, t: min(L, L - Q + t + 2)),
     "no causal mask": ("visible_count", lambda L, Q, t: L),
