@@ -70,7 +70,17 @@ typedef struct {
   int64_t num_slots;  /* rows in kv_pool (>= 1) */
   float sm_scale;     /* score scale, > 0 (1/sqrt(192) in the reference workloads) */
   int32_t form;       /* kernel-1 layout: MLA_VERIFY_FORM_AUTO (0), _128ROW (1) or _TWO_STREAM (2) */
+  int32_t flags;      /* OR of MLA_VERIFY_FLAG_* (0: none) */
 } mla_verify_config;
+
+/* Batch invariance: a request's out and lse are bit for bit the same whatever other requests
+ * share its call (and whatever the batch size of the handle), as long as the handle's max_q_len,
+ * num_heads, form and the call's nsplit are the same.  Without it, batches of 2..64 requests
+ * (of more than 64 rows each) spread their keys over the CUs by the range plan described at
+ * mla_verify_run, which moves split boundaries with the batch and so changes rounding; the flag
+ * turns the range plan off (each request is split on its own), at some cost in speed for ragged
+ * batches.  Any other bit is INVALID_ARGUMENT. */
+#define MLA_VERIFY_FLAG_BATCH_INVARIANT 1
 
 /* Kernel-1 layouts (the result is the same up to rounding; they differ in speed).
  * 128ROW: workgroups of 128 (draft token, head) rows, one 32-key tile per step.
@@ -89,7 +99,7 @@ typedef struct {
  * (B * max_nsplit * ceil(Q_max*H/128)*128 rows of 512 bf16 partial outputs,
  * each normalised within its split, plus one fp32 log-sum-exp each) and
  * return a handle in *out.  Call outside graph capture.
- * Errors: INVALID_ARGUMENT (null, non-positive sizes), UNSUPPORTED (dims),
+ * Errors: INVALID_ARGUMENT (null, non-positive sizes, unknown form or flag), UNSUPPORTED (dims),
  * OUT_OF_MEMORY, HIP (no device).  On error *out is set to NULL.
  */
 int mla_verify_create(const mla_verify_config* cfg, mla_verify_handle* out);

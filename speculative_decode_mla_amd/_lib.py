@@ -18,6 +18,7 @@ MLA_ERR_HIP = -4
 FORM_AUTO = 0        # kernel-1 layouts (include/mla_verify.h)
 FORM_128ROW = 1
 FORM_TWO_STREAM = 2
+FLAG_BATCH_INVARIANT = 1  # create flags (include/mla_verify.h)
 
 D_QK = 576
 D_V = 512
@@ -38,6 +39,7 @@ class MlaVerifyConfig(ctypes.Structure):
         ("num_slots", ctypes.c_int64),
         ("sm_scale", ctypes.c_float),
         ("form", ctypes.c_int32),
+        ("flags", ctypes.c_int32),
     ]
 
 

@@ -47,13 +47,16 @@ class MlaVerify:
     without synchronising, so it can be captured in a torch.cuda.CUDAGraph.
     `form` picks kernel 1's layout (FORM_AUTO, FORM_128ROW or FORM_TWO_STREAM from
     _lib); the result is the same up to rounding, only the speed differs.
+    `batch_invariant` makes each request's result bitwise independent of its batchmates
+    (MLA_VERIFY_FLAG_BATCH_INVARIANT: no range plan).
     """
 
     def __init__(self, num_heads: int, batch: int, max_q_len: int, max_nsplit: int, num_slots: int,
-                 sm_scale: float = DEFAULT_SCALE, form: int = _lib.FORM_AUTO):
+                 sm_scale: float = DEFAULT_SCALE, form: int = _lib.FORM_AUTO, batch_invariant: bool = False):
         lib = _lib.load()
+        flags = _lib.FLAG_BATCH_INVARIANT if batch_invariant else 0
         self.cfg = _lib.MlaVerifyConfig(num_heads, D_QK, D_V, batch, max_q_len, max_nsplit, num_slots, sm_scale,
-                                        form)
+                                        form, flags)
         h = ctypes.c_void_p()
         _lib.check("mla_verify_create", lib.mla_verify_create(ctypes.byref(self.cfg), ctypes.byref(h)))
         self._h = h

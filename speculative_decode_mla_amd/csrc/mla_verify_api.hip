@@ -35,6 +35,79 @@ int hip_status(hipError_t e) {
   return e == hipErrorOutOfMemory ? MLA_ERR_OUT_OF_MEMORY : MLA_ERR_HIP;
 }
 
+// Validate a config without any HIP call.
+int validate_config(const mla_verify_config* cfg) {
+  if (cfg == nullptr) return MLA_ERR_INVALID_ARGUMENT;
+  if (cfg->num_heads < 1 || cfg->batch < 1 || cfg->max_q_len < 1 || cfg->max_nsplit < 1 || cfg->num_slots < 1)
+    return MLA_ERR_INVALID_ARGUMENT;
+  if (!(cfg->sm_scale > 0.f) || !std::isfinite(cfg->sm_scale)) return MLA_ERR_INVALID_ARGUMENT;
+  if (cfg->d_qk != MLA_VERIFY_D_QK || cfg->d_v != MLA_VERIFY_D_V) return MLA_ERR_UNSUPPORTED;
+  if (cfg->form != MLA_VERIFY_FORM_AUTO && cfg->form != MLA_VERIFY_FORM_128ROW &&
+      cfg->form != MLA_VERIFY_FORM_TWO_STREAM)
+    return MLA_ERR_INVALID_ARGUMENT;
+  if ((cfg->flags & ~MLA_VERIFY_FLAG_BATCH_INVARIANT) != 0) return MLA_ERR_INVALID_ARGUMENT;
+  const int64_t rows = (int64_t)cfg->max_q_len * cfg->num_heads;
+  const int64_t grid = (int64_t)cfg->batch * cfg->max_nsplit * ((rows + mlav::kRowsPerGroup2s - 1) / mlav::kRowsPerGroup2s);
+  if (rows > INT32_MAX / 2 || grid > INT32_MAX || (int64_t)cfg->batch * rows > INT32_MAX)
+    return MLA_ERR_INVALID_ARGUMENT;
+  return MLA_OK;
+}
+
+// Kernel-1 form of a config before the per-call choice: 1 (128-row workgroups) or 2 (two streams).
+int32_t config_streams(const mla_verify_config* cfg) {
+  const int64_t rows = (int64_t)cfg->max_q_len * cfg->num_heads;
+  // Requests of at most 64 rows (a q_len = 1 decode step with H <= 64) use the two-stream form of
+  // kernel 1, whose workgroups hold 64 rows; larger ones the 128-row form (or, per call, the
+  // two-stream form when the 128-row workgroups would leave most CUs idle; see launch_partials).
+  return cfg->form == MLA_VERIFY_FORM_TWO_STREAM ? 2
+         : cfg->form == MLA_VERIFY_FORM_128ROW   ? 1
+         : rows <= mlav::kRowsPerGroup2s        ? 2 : 1;
+}
+
+// Workspace rows per partial: rows past 64 are padded to a multiple of 128, which holds the row
+// groups of either form.
+int64_t config_rows_pad(const mla_verify_config* cfg) {
+  const int64_t rows = (int64_t)cfg->max_q_len * cfg->num_heads;
+  const int64_t group = config_streams(cfg) == 2 ? mlav::kRowsPerGroup2s : mlav::kRowsPerGroup;
+  return rows <= mlav::kRowsPerGroup2s ? (rows + group - 1) / group * group
+                                       : (rows + mlav::kRowsPerGroup - 1) / mlav::kRowsPerGroup * mlav::kRowsPerGroup;
+}
+
+// Fill every field of a handle but the workspace pointers (null) from a validated config and the
+// device's CU count: the kernel-1 form, the row groups, the range plan.  No HIP call.
+void fill_geometry(const mla_verify_config* cfg, int dev, int cus, mla_verify_s* h) {
+  const int64_t rows = (int64_t)cfg->max_q_len * cfg->num_heads;
+  const int32_t streams = config_streams(cfg);
+  const int64_t group = streams == 2 ? mlav::kRowsPerGroup2s : mlav::kRowsPerGroup;
+  const int64_t row_groups = (rows + group - 1) / group;
+  h->cfg = *cfg;
+  h->device = dev;
+  h->row_groups = (int32_t)row_groups;
+  h->rows_pad = (int32_t)config_rows_pad(cfg);
+  h->streams = streams;
+  h->rows = (int32_t)rows;
+  h->cus = cus;
+  // A batch in the 128-row form is spread over one workgroup per CU (one resident per CU), as
+  // `workers` workers of row_groups workgroups each (the range plan of kernel 1), unless the
+  // caller asked for results independent of the batch composition.
+  h->plan_ranges = streams == 1 && cfg->batch >= 2 && cfg->batch <= mlav::kRangeMaxBatch && row_groups <= cus &&
+                   (cfg->flags & MLA_VERIFY_FLAG_BATCH_INVARIANT) == 0;
+  // (a multiple of 8 from 8 workers on, so that each XCD takes the same share and holds at most
+  // 64 workers, one per lane of the planner's wave)
+  const int64_t workers = cus / row_groups;
+  h->workers = h->plan_ranges ? (int32_t)(workers >= 8 ? workers & ~int64_t(7) : workers) : 0;
+  h->o_part = nullptr;
+  h->lse_part = nullptr;
+}
+
+// The current device and its CU count.
+int current_device(int* dev, int* cus) {
+  if (hipGetDevice(dev) != hipSuccess) return MLA_ERR_HIP;
+  if (hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, *dev) != hipSuccess || *cus < 1)
+    return MLA_ERR_HIP;
+  return MLA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -53,53 +126,17 @@ const char* mla_verify_error_string(int status) {
 int mla_verify_create(const mla_verify_config* cfg, mla_verify_handle* out) {
   if (out == nullptr) return MLA_ERR_INVALID_ARGUMENT;
   *out = nullptr;
-  if (cfg == nullptr) return MLA_ERR_INVALID_ARGUMENT;
-  if (cfg->num_heads < 1 || cfg->batch < 1 || cfg->max_q_len < 1 || cfg->max_nsplit < 1 || cfg->num_slots < 1)
-    return MLA_ERR_INVALID_ARGUMENT;
-  if (!(cfg->sm_scale > 0.f) || !std::isfinite(cfg->sm_scale)) return MLA_ERR_INVALID_ARGUMENT;
-  if (cfg->d_qk != MLA_VERIFY_D_QK || cfg->d_v != MLA_VERIFY_D_V) return MLA_ERR_UNSUPPORTED;
-  if (cfg->form != MLA_VERIFY_FORM_AUTO && cfg->form != MLA_VERIFY_FORM_128ROW &&
-      cfg->form != MLA_VERIFY_FORM_TWO_STREAM)
-    return MLA_ERR_INVALID_ARGUMENT;
-  const int64_t rows = (int64_t)cfg->max_q_len * cfg->num_heads;
-  // Requests of at most 64 rows (a q_len = 1 decode step with H <= 64) use the two-stream form of
-  // kernel 1, whose workgroups hold 64 rows; larger ones the 128-row form (or, per call, the
-  // two-stream form when the 128-row workgroups would leave most CUs idle; see launch_partials).
-  const int32_t streams = cfg->form == MLA_VERIFY_FORM_TWO_STREAM ? 2
-                          : cfg->form == MLA_VERIFY_FORM_128ROW   ? 1
-                          : rows <= mlav::kRowsPerGroup2s        ? 2 : 1;
-  const int64_t group = streams == 2 ? mlav::kRowsPerGroup2s : mlav::kRowsPerGroup;
-  const int64_t row_groups = (rows + group - 1) / group;
-  // (rows past 64 are padded to a multiple of 128, which holds the groups of either form)
-  const int64_t rows_pad = rows <= mlav::kRowsPerGroup2s ? row_groups * group
-                                                         : (rows + mlav::kRowsPerGroup - 1) / mlav::kRowsPerGroup * mlav::kRowsPerGroup;
-  const int64_t grid = (int64_t)cfg->batch * cfg->max_nsplit * ((rows + mlav::kRowsPerGroup2s - 1) / mlav::kRowsPerGroup2s);
-  if (rows_pad > INT32_MAX / 2 || grid > INT32_MAX || (int64_t)cfg->batch * rows > INT32_MAX)
-    return MLA_ERR_INVALID_ARGUMENT;
-
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return MLA_ERR_HIP;
-  int cus = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
-    return MLA_ERR_HIP;
-  const int64_t partial_rows = (int64_t)cfg->batch * cfg->max_nsplit * rows_pad;
-  mla_verify_s* h = new (std::nothrow) mla_verify_s();
+  int st = validate_config(cfg);
+  if (st != MLA_OK) return st;
+  int dev = 0, cus = 0;
+  st = current_device(&dev, &cus);
+  if (st != MLA_OK) return st;
+  mla_verify_s geo;
+  fill_geometry(cfg, dev, cus, &geo);
+  const int64_t partial_rows = (int64_t)cfg->batch * cfg->max_nsplit * geo.rows_pad;
+  mla_verify_s* h = new (std::nothrow) mla_verify_s(geo);
   if (h == nullptr) return MLA_ERR_OUT_OF_MEMORY;
-  h->cfg = *cfg;
-  h->device = dev;
-  h->row_groups = (int32_t)row_groups;
-  h->rows_pad = (int32_t)rows_pad;
-  h->streams = streams;
-  h->rows = (int32_t)rows;
-  h->cus = cus;
-  // A batch in the 128-row form is spread over one workgroup per CU (one resident per CU), as
-  // `workers` workers of row_groups workgroups each (the range plan of kernel 1).
-  h->plan_ranges = streams == 1 && cfg->batch >= 2 && cfg->batch <= mlav::kRangeMaxBatch && row_groups <= cus;
-  // (a multiple of 8 from 8 workers on, so that each XCD takes the same share and holds at most
-  // 64 workers, one per lane of the planner's wave)
-  const int64_t workers = cus / row_groups;
-  h->workers = h->plan_ranges ? (int32_t)(workers >= 8 ? workers & ~int64_t(7) : workers) : 0;
-  int st = hip_status(hipMalloc((void**)&h->o_part, (size_t)partial_rows * mlav::kDv * sizeof(uint16_t)));
+  st = hip_status(hipMalloc((void**)&h->o_part, (size_t)partial_rows * mlav::kDv * sizeof(uint16_t)));
   if (st == MLA_OK) st = hip_status(hipMalloc((void**)&h->lse_part, (size_t)partial_rows * sizeof(float)));
   if (st != MLA_OK) {
     (void)hipGetLastError();
@@ -147,8 +184,11 @@ int launch_partials(mla_verify_handle h, const void* q, const void* kv_pool, con
   // splits, e.g. nsplit 16 with 8 row groups) takes the two-stream form instead: 64-row workgroups,
   // twice as many, over the same splits, so the partials (and the merge) are the same.  (Decided
   // from the call's shape alone; kernel 1 may still leave splits of short requests empty.)
+  // With MLA_VERIFY_FLAG_BATCH_INVARIANT the choice is made as for one request, so that it does
+  // not depend on the batch size either.
+  const int64_t form_batch = (c.flags & MLA_VERIFY_FLAG_BATCH_INVARIANT) ? 1 : c.batch;
   if (c.form == MLA_VERIFY_FORM_AUTO && pa.streams == 1 && !h->plan_ranges &&
-      2 * (int64_t)c.batch * nsplit * h->row_groups <= h->cus) {
+      2 * form_batch * nsplit * h->row_groups <= h->cus) {
     pa.streams = 2;
     pa.row_groups = (h->rows + mlav::kRowsPerGroup2s - 1) / mlav::kRowsPerGroup2s;  // rows_pad (a multiple of 128) holds them
   }
@@ -167,14 +207,13 @@ int mla_verify_partials(mla_verify_handle h, const void* q, const void* kv_pool,
   return launch_partials(h, q, kv_pool, slot_idx, seq_lens, q_lens, nsplit, static_cast<hipStream_t>(stream));
 }
 
-int mla_verify_run(mla_verify_handle h, const void* q, const void* kv_pool, const int32_t* slot_idx,
-                   const int32_t* seq_lens, const int32_t* q_lens, void* out, float* lse, int32_t nsplit,
-                   void* stream) {
-  int st = check_run_args(h, q, kv_pool, slot_idx, seq_lens, q_lens, nsplit);
-  if (st != MLA_OK) return st;
-  if (out == nullptr || lse == nullptr || !aligned(out, 16) || !aligned(lse, 4)) return MLA_ERR_INVALID_ARGUMENT;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  st = launch_partials(h, q, kv_pool, slot_idx, seq_lens, q_lens, nsplit, s);
+namespace {
+
+// The two launches of a verify call on a handle whose arguments have been checked.
+int enqueue_run(mla_verify_handle h, const void* q, const void* kv_pool, const int32_t* slot_idx,
+                const int32_t* seq_lens, const int32_t* q_lens, void* out, float* lse, int32_t nsplit,
+                hipStream_t s) {
+  int st = launch_partials(h, q, kv_pool, slot_idx, seq_lens, q_lens, nsplit, s);
   if (st != MLA_OK) return st;
 
   const mla_verify_config& c = h->cfg;
@@ -196,6 +235,17 @@ int mla_verify_run(mla_verify_handle h, const void* q, const void* kv_pool, cons
   ma.plan_ranges = h->plan_ranges;
   ma.workers = h->workers;
   return mlav::launch_merge(ma, s) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+}  // namespace
+
+int mla_verify_run(mla_verify_handle h, const void* q, const void* kv_pool, const int32_t* slot_idx,
+                   const int32_t* seq_lens, const int32_t* q_lens, void* out, float* lse, int32_t nsplit,
+                   void* stream) {
+  int st = check_run_args(h, q, kv_pool, slot_idx, seq_lens, q_lens, nsplit);
+  if (st != MLA_OK) return st;
+  if (out == nullptr || lse == nullptr || !aligned(out, 16) || !aligned(lse, 4)) return MLA_ERR_INVALID_ARGUMENT;
+  return enqueue_run(h, q, kv_pool, slot_idx, seq_lens, q_lens, out, lse, nsplit, static_cast<hipStream_t>(stream));
 }
 
 int mla_verify_merge(const float* o_part, const float* lse_part, const int32_t* q_lens, int32_t batch,

@@ -40,8 +40,9 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_config_struct_layout_matches_header():
-    assert ctypes.sizeof(_lib.MlaVerifyConfig) == 40
+    assert ctypes.sizeof(_lib.MlaVerifyConfig) == 48
     assert _lib.MlaVerifyConfig.num_slots.offset == 24 and _lib.MlaVerifyConfig.sm_scale.offset == 32
+    assert _lib.MlaVerifyConfig.form.offset == 36 and _lib.MlaVerifyConfig.flags.offset == 40
 
 
 def test_error_strings(lib):

@@ -163,6 +163,37 @@ def test_slot_permutation_is_bitwise(api):
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
+@pytest.mark.parametrize("seed,lens,qlens,heads,nsplit,member", [
+    (34, [500, 1200, 90], [4, 16, 2], 8, 6, 1),          # range plan without the flag
+    (67, [3000, 20000, 700, 65], [16, 16, 16, 9], 64, 32, 1),  # 128-row form per request
+    (68, [9000, 400], [16, 16], 64, 8, 0),               # two-stream form chosen as for one request
+    (69, [2000, 3000], [1, 1], 64, 16, 1),               # decode rows
+])
+def test_batch_invariant_request_is_bitwise_alone(api, seed, lens, qlens, heads, nsplit, member):
+    """With MLA_VERIFY_FLAG_BATCH_INVARIANT a request's out and lse are bit for bit the same alone
+    (a one-request handle) and inside a batch (the batch-composition pin, bitwise)."""
+    x = I.make_custom(np.random.default_rng(seed), lens, qlens, heads, int(sum(lens)) * 2 + 64)
+    max_q = int(max(qlens))
+    d = DeviceInputs(x)
+    h = api.MlaVerify(heads, len(lens), max_q, nsplit, x.num_slots, x.scale, batch_invariant=True)
+    out, lse = d.run(h, nsplit)
+    torch.cuda.synchronize()
+    ko = int(sum(lens[:member]))
+    qo = int(sum(qlens[:member]))
+    L, Q = lens[member], qlens[member]
+    y = I.VerifyInputs(q=x.q[qo:qo + Q], kv_rows=x.kv_rows[ko:ko + L], slot_idx=x.slot_idx[ko:ko + L],
+                       seq_lens=x.seq_lens[member:member + 1], q_lens=x.q_lens[member:member + 1],
+                       num_slots=x.num_slots, heads=heads)
+    e = DeviceInputs(y)
+    o1, l1 = e.run(api.MlaVerify(heads, 1, max_q, nsplit, x.num_slots, x.scale, batch_invariant=True), nsplit)
+    torch.cuda.synchronize()
+    assert torch.equal(out[qo:qo + Q].view(torch.int16), o1.view(torch.int16))
+    assert torch.equal(lse[qo:qo + Q], l1)
+    ref_o, ref_l = oracle.verify_attention(y.q, y.pool(), y.slot_idx, y.seq_lens, y.q_lens, y.scale)
+    eo, el = max_errors(o1, l1, ref_o, ref_l)
+    assert eo <= OUT_TOL and el <= LSE_TOL
+
+
 def test_request_alone_equals_request_in_batch(api):
     x = I.make_custom(np.random.default_rng(34), [500, 1200, 90], [4, 16, 2], 8, 4000)
     d = DeviceInputs(x)
