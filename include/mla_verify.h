@@ -53,6 +53,7 @@ extern "C" {
 #define MLA_ERR_UNSUPPORTED (-2)      /* d_qk != 576 or d_v != 512 */
 #define MLA_ERR_OUT_OF_MEMORY (-3)    /* workspace allocation failed */
 #define MLA_ERR_HIP (-4)              /* a HIP runtime call or a kernel launch failed, or no GPU */
+#define MLA_ERR_SCRATCH_TOO_SMALL (-5) /* mla_verify_run_noalloc: the call's partials exceed its fixed scratch */
 
 #define MLA_VERIFY_D_QK 576 /* 512 latent + 64 rope dims per cached row and per query */
 #define MLA_VERIFY_D_V 512  /* v is the first 512 dims of each cached row */
@@ -131,6 +132,31 @@ int mla_verify_create(const mla_verify_config* cfg, mla_verify_handle* out);
 int mla_verify_run(mla_verify_handle h, const void* q, const void* kv_pool, const int32_t* slot_idx,
                    const int32_t* seq_lens, const int32_t* q_lens, void* out, float* lse, int32_t nsplit,
                    void* stream);
+
+/*
+ * mla_verify_run without a handle and without any allocation, for callers that cannot allocate
+ * device memory at the time of the call (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The same kernels and the same result as mla_verify_run on a
+ * handle created from *cfg (bit for bit), but the split partials live in a fixed device array
+ * inside the library, MLA_VERIFY_NOALLOC_SCRATCH_BYTES (40 MiB) per GPU, which each GPU the
+ * library runs on holds from the first use until the process ends.
+ *   cfg      the shapes, as for mla_verify_create (read on every call; not kept).
+ *   other arguments as in mla_verify_run; nsplit <= cfg->max_nsplit.
+ * Size limit: B * nsplit * rows_pad * 512 bf16 partials (rows_pad = ceil(Q_max*H/128)*128, or 64
+ * when Q_max*H <= 64), then B * nsplit * rows_pad fp32 LSEs from the next 256-B boundary, must fit
+ * the array; otherwise MLA_ERR_SCRATCH_TOO_SMALL and nothing is enqueued.  (One request of 1,024
+ * rows at nsplit 32 takes 32.1 MiB; a 64-row decode step at nsplit 256 takes 16.1 MiB.)
+ * Every call on one GPU uses that GPU's one array: calls that overlap in time on one GPU (other
+ * streams, other threads, other handles' noalloc calls) race on it and give wrong results;
+ * serialise them.  Nothing in the array needs to start at zero (every partial read is written
+ * by the same call).  The first call on each device looks up the array's device address
+ * (hipGetSymbolAddress, no allocation); make that first call outside graph capture.
+ * Errors: INVALID_ARGUMENT, UNSUPPORTED (as for create), SCRATCH_TOO_SMALL, HIP.
+ */
+#define MLA_VERIFY_NOALLOC_SCRATCH_BYTES (40u << 20)
+int mla_verify_run_noalloc(const mla_verify_config* cfg, const void* q, const void* kv_pool,
+                           const int32_t* slot_idx, const int32_t* seq_lens, const int32_t* q_lens, void* out,
+                           float* lse, int32_t nsplit, void* stream);
 
 /*
  * Kernel 1 alone: the split partials of one call, left in the handle's

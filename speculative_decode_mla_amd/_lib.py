@@ -14,6 +14,8 @@ MLA_ERR_INVALID_ARGUMENT = -1
 MLA_ERR_UNSUPPORTED = -2
 MLA_ERR_OUT_OF_MEMORY = -3
 MLA_ERR_HIP = -4
+MLA_ERR_SCRATCH_TOO_SMALL = -5
+NOALLOC_SCRATCH_BYTES = 40 << 20  # MLA_VERIFY_NOALLOC_SCRATCH_BYTES
 
 FORM_AUTO = 0        # kernel-1 layouts (include/mla_verify.h)
 FORM_128ROW = 1
@@ -46,6 +48,8 @@ class MlaVerifyConfig(ctypes.Structure):
 SIGNATURES = {
     "mla_verify_create": (ctypes.c_int, [ctypes.POINTER(MlaVerifyConfig), ctypes.POINTER(_P)]),
     "mla_verify_run": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _P]),
+    "mla_verify_run_noalloc": (ctypes.c_int, [ctypes.POINTER(MlaVerifyConfig), _P, _P, _P, _P, _P, _P, _P, _I32,
+                                              _P]),
     "mla_verify_partials": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I32, _P]),
     "mla_verify_merge": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _P]),
     "mla_verify_compact": (ctypes.c_int, [_P, _P, ctypes.c_int64, _P, ctypes.c_int64, ctypes.c_int64, _P, _P]),

@@ -130,6 +130,34 @@ class MlaVerify:
         return out, lse
 
 
+def run_noalloc(q, kv_pool, slot_idx, seq_lens, q_lens, out, lse, nsplit: int, num_heads: int, batch: int,
+                max_q_len: int, max_nsplit: int, num_slots: int, sm_scale: float = DEFAULT_SCALE,
+                form: int = _lib.FORM_AUTO, batch_invariant: bool = False, stream=None):
+    """mla_verify_run_noalloc: one verify call with no handle and no allocation (the split partials
+    live in the library's fixed per-GPU scratch array).  Shapes as for MlaVerify(...).run(...)."""
+    _need(q, "q", torch.bfloat16, 3)
+    _need(kv_pool, "kv_pool", torch.bfloat16, 2)
+    _need(slot_idx, "slot_idx", torch.int32, 1)
+    _need(seq_lens, "seq_lens", torch.int32, 1)
+    _need(q_lens, "q_lens", torch.int32, 1)
+    _need(out, "out", torch.bfloat16, 3)
+    _need(lse, "lse", torch.float32, 2)
+    if q.shape[1:] != (num_heads, D_QK) or out.shape != (q.shape[0], num_heads, D_V) or \
+            lse.shape != (q.shape[0], num_heads):
+        raise ValueError("q, out and lse must be [T_q, H, 576], [T_q, H, 512] and [T_q, H]")
+    if kv_pool.shape[1] != D_QK or kv_pool.shape[0] > num_slots:
+        raise ValueError(f"kv_pool must be [<= {num_slots}, {D_QK}], got {tuple(kv_pool.shape)}")
+    if seq_lens.shape[0] != batch or q_lens.shape[0] != batch:
+        raise ValueError(f"seq_lens and q_lens must have {batch} entries")
+    cfg = _lib.MlaVerifyConfig(num_heads, D_QK, D_V, batch, max_q_len, max_nsplit, num_slots, sm_scale, form,
+                               _lib.FLAG_BATCH_INVARIANT if batch_invariant else 0)
+    st = _lib.load().mla_verify_run_noalloc(ctypes.byref(cfg), _ptr(q), _ptr(kv_pool), _ptr(slot_idx),
+                                            _ptr(seq_lens), _ptr(q_lens), _ptr(out), _ptr(lse), int(nsplit),
+                                            _stream_handle(stream))
+    _lib.check("mla_verify_run_noalloc", st)
+    return out, lse
+
+
 def compact(kv_pool, slot_idx, dst_pool, dst_first: int, new_slot_idx=None, stream=None):
     """KV compaction: dst_pool[dst_first + j] = kv_pool[slot_idx[j]]; new_slot_idx[j] = dst_first + j.
 

@@ -4,6 +4,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 #include <new>
 
 #include "mla_verify_internal.h"
@@ -119,6 +120,7 @@ const char* mla_verify_error_string(int status) {
     case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED";
     case MLA_ERR_OUT_OF_MEMORY: return "MLA_ERR_OUT_OF_MEMORY";
     case MLA_ERR_HIP: return "MLA_ERR_HIP";
+    case MLA_ERR_SCRATCH_TOO_SMALL: return "MLA_ERR_SCRATCH_TOO_SMALL";
     default: return "MLA_ERR_UNKNOWN";
   }
 }
@@ -146,6 +148,8 @@ int mla_verify_create(const mla_verify_config* cfg, mla_verify_handle* out) {
   *out = h;
   return MLA_OK;
 }
+
+}  // extern "C"
 
 namespace {
 
@@ -200,6 +204,8 @@ int launch_partials(mla_verify_handle h, const void* q, const void* kv_pool, con
 
 }  // namespace
 
+extern "C" {
+
 int mla_verify_partials(mla_verify_handle h, const void* q, const void* kv_pool, const int32_t* slot_idx,
                         const int32_t* seq_lens, const int32_t* q_lens, int32_t nsplit, void* stream) {
   int st = check_run_args(h, q, kv_pool, slot_idx, seq_lens, q_lens, nsplit);
@@ -207,7 +213,37 @@ int mla_verify_partials(mla_verify_handle h, const void* q, const void* kv_pool,
   return launch_partials(h, q, kv_pool, slot_idx, seq_lens, q_lens, nsplit, static_cast<hipStream_t>(stream));
 }
 
+}  // extern "C"
+
 namespace {
+
+// ---- The entry point that allocates nothing (mla_verify_run_noalloc) --------------------------------
+// Its split workspace is this file-scope device array: every GPU the library runs on holds its own
+// copy (MLA_VERIFY_NOALLOC_SCRATCH_BYTES) from the first use until the process ends.  In host code
+// `scratch` names a host-side stand-in, not device memory; the device address of the current GPU's
+// copy comes from hipGetSymbolAddress, once per device, and only that address is handed to kernels.
+static_assert(MLA_VERIFY_NOALLOC_SCRATCH_BYTES % 256 == 0, "lse partials start 256-B aligned");
+static __device__ __align__(256) char scratch[MLA_VERIFY_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` on device d (null until looked up)
+
+// The current device's scratch address, looked up on the first call on that device.
+int device_scratch(int dev, void** ptr) {
+  if (dev < 0 || dev >= kMaxDevices) return MLA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+      (void)hipGetLastError();
+      return MLA_ERR_HIP;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return MLA_OK;
+}
 
 // The two launches of a verify call on a handle whose arguments have been checked.
 int enqueue_run(mla_verify_handle h, const void* q, const void* kv_pool, const int32_t* slot_idx,
@@ -239,6 +275,8 @@ int enqueue_run(mla_verify_handle h, const void* q, const void* kv_pool, const i
 
 }  // namespace
 
+extern "C" {
+
 int mla_verify_run(mla_verify_handle h, const void* q, const void* kv_pool, const int32_t* slot_idx,
                    const int32_t* seq_lens, const int32_t* q_lens, void* out, float* lse, int32_t nsplit,
                    void* stream) {
@@ -246,6 +284,38 @@ int mla_verify_run(mla_verify_handle h, const void* q, const void* kv_pool, cons
   if (st != MLA_OK) return st;
   if (out == nullptr || lse == nullptr || !aligned(out, 16) || !aligned(lse, 4)) return MLA_ERR_INVALID_ARGUMENT;
   return enqueue_run(h, q, kv_pool, slot_idx, seq_lens, q_lens, out, lse, nsplit, static_cast<hipStream_t>(stream));
+}
+
+int mla_verify_run_noalloc(const mla_verify_config* cfg, const void* q, const void* kv_pool,
+                           const int32_t* slot_idx, const int32_t* seq_lens, const int32_t* q_lens, void* out,
+                           float* lse, int32_t nsplit, void* stream) {
+  int st = validate_config(cfg);
+  if (st != MLA_OK) return st;
+  if (q == nullptr || kv_pool == nullptr || slot_idx == nullptr || seq_lens == nullptr || q_lens == nullptr ||
+      out == nullptr || lse == nullptr)
+    return MLA_ERR_INVALID_ARGUMENT;
+  if (nsplit < 1 || nsplit > cfg->max_nsplit) return MLA_ERR_INVALID_ARGUMENT;
+  if (!aligned(q, 16) || !aligned(kv_pool, 16) || !aligned(slot_idx, 4) || !aligned(seq_lens, 4) ||
+      !aligned(q_lens, 4) || !aligned(out, 16) || !aligned(lse, 4))
+    return MLA_ERR_INVALID_ARGUMENT;
+  // The call's partials, laid out as in a handle's workspace for this nsplit: bf16 rows, then fp32
+  // LSEs from the next 256-B boundary.
+  const int64_t partial_rows = (int64_t)cfg->batch * nsplit * config_rows_pad(cfg);
+  const int64_t o_bytes = partial_rows * mlav::kDv * (int64_t)sizeof(uint16_t);
+  const int64_t lse_offset = (o_bytes + 255) / 256 * 256;
+  if (lse_offset + partial_rows * (int64_t)sizeof(float) > (int64_t)MLA_VERIFY_NOALLOC_SCRATCH_BYTES)
+    return MLA_ERR_SCRATCH_TOO_SMALL;
+  int dev = 0, cus = 0;
+  st = current_device(&dev, &cus);
+  if (st != MLA_OK) return st;
+  void* base = nullptr;
+  st = device_scratch(dev, &base);
+  if (st != MLA_OK) return st;
+  mla_verify_s h;
+  fill_geometry(cfg, dev, cus, &h);
+  h.o_part = static_cast<uint16_t*>(base);
+  h.lse_part = reinterpret_cast<float*>(static_cast<char*>(base) + lse_offset);
+  return enqueue_run(&h, q, kv_pool, slot_idx, seq_lens, q_lens, out, lse, nsplit, static_cast<hipStream_t>(stream));
 }
 
 int mla_verify_merge(const float* o_part, const float* lse_part, const int32_t* q_lens, int32_t batch,

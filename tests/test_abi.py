@@ -27,7 +27,8 @@ def lib():
 def test_header_declares_the_boundary():
     assert _declared() == ["mla_verify_build_metadata", "mla_verify_compact", "mla_verify_create",
                            "mla_verify_destroy", "mla_verify_error_string", "mla_verify_merge",
-                           "mla_verify_partials", "mla_verify_run", "mla_verify_workspace"]
+                           "mla_verify_partials", "mla_verify_run", "mla_verify_run_noalloc",
+                           "mla_verify_workspace"]
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -111,3 +112,20 @@ def test_torch_wrapper_rejects_bad_tensors():
         api._need(torch.zeros(3, 4, dtype=torch.bfloat16).t(), "x", torch.bfloat16, 2)
     with pytest.raises(ValueError):
         api._need(torch.zeros(3, dtype=torch.bfloat16), "x", torch.bfloat16, 1)  # not on a GPU
+
+
+def test_noalloc_rejects_what_its_scratch_cannot_hold(lib):
+    """mla_verify_run_noalloc checks the call's partials against its fixed scratch before any HIP call."""
+    P = ctypes.c_void_p
+    dummy = P(1 << 20)  # never dereferenced: every call below is rejected on the host
+    cfg = _lib.MlaVerifyConfig(64, 576, 512, 16, 16, 32, 1 << 22, 0.072, 0, 0)  # batch16: 16 x 32 x 1024 rows
+    assert lib.mla_verify_run_noalloc(ctypes.byref(cfg), dummy, dummy, dummy, dummy, dummy, dummy, dummy, 32,
+                                      None) == _lib.MLA_ERR_SCRATCH_TOO_SMALL
+    cfg = _lib.MlaVerifyConfig(64, 576, 512, 1, 16, 64, 1 << 21, 0.072, 0, 0)    # 1,024 rows at nsplit 40
+    assert lib.mla_verify_run_noalloc(ctypes.byref(cfg), dummy, dummy, dummy, dummy, dummy, dummy, dummy, 40,
+                                      None) == _lib.MLA_ERR_SCRATCH_TOO_SMALL
+    assert lib.mla_verify_run_noalloc(ctypes.byref(cfg), dummy, dummy, dummy, dummy, dummy, dummy, dummy, 65,
+                                      None) == _lib.MLA_ERR_INVALID_ARGUMENT       # nsplit > max_nsplit
+    assert lib.mla_verify_run_noalloc(None, dummy, dummy, dummy, dummy, dummy, dummy, dummy, 1,
+                                      None) == _lib.MLA_ERR_INVALID_ARGUMENT
+    assert _lib.error_string(_lib.MLA_ERR_SCRATCH_TOO_SMALL) == "MLA_ERR_SCRATCH_TOO_SMALL"
