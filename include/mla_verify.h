@@ -258,6 +258,29 @@ int mla_verify_build_metadata(const int32_t* req_to_token, int32_t table_rows, i
 int mla_verify_workspace(mla_verify_handle h, void** o_part, int64_t* o_part_bytes, void** lse_part,
                          int64_t* lse_part_bytes);
 
+/*
+ * Checks of device-visible arguments (slot_idx, seq_lens and q_lens are read only on the device,
+ * so a release build cannot reject them).  libmla_verify_debug.so is
+ * the same library built with MLA_VERIFY_DEBUG defined: its verify kernels replace a bad value
+ * before it is used for any memory access and OR a bit into a device word of the handle:
+ *   MLA_VERIFY_DEBUG_SLOT_OUT_OF_RANGE   a slot outside [0, num_slots): clamped into it;
+ *   MLA_VERIFY_DEBUG_NEGATIVE_LENGTH     seq_lens[b] < 0: read as 0 (then request b has no
+ *                                        keys and no rows, and takes no slots);
+ *   MLA_VERIFY_DEBUG_Q_LEN_OUT_OF_RANGE  q_lens[b] outside [0, min(seq_lens[b], max_q_len)]:
+ *                                        clamped (the release build clamps it silently).
+ * The results of such a call are whatever the clamped arguments give; the point is that no
+ * access leaves the caller's buffers (given a pool of num_slots rows) and that the caller can
+ * find out.  mla_verify_debug_flags synchronises the device, stores the word in *flags (0: no
+ * check fired since creation or the last clear) and, if `clear` is non-zero, resets it.  In the
+ * release library it stores 0 and returns MLA_ERR_UNSUPPORTED.  (mla_verify_run_noalloc clamps
+ * the same way in the debug build but has no handle to keep a word in.)
+ * Errors: INVALID_ARGUMENT (null), UNSUPPORTED (release build), HIP.
+ */
+#define MLA_VERIFY_DEBUG_SLOT_OUT_OF_RANGE 1
+#define MLA_VERIFY_DEBUG_NEGATIVE_LENGTH 2
+#define MLA_VERIFY_DEBUG_Q_LEN_OUT_OF_RANGE 4
+int mla_verify_debug_flags(mla_verify_handle h, int32_t* flags, int32_t clear);
+
 /* Free the workspace and the handle.  NULL is a no-op.  The caller must make
  * sure no enqueued call still uses the handle (synchronise its stream first). */
 int mla_verify_destroy(mla_verify_handle h);

@@ -8,6 +8,11 @@ import ctypes
 import os
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla_verify.so")
+# the same library with the device-side argument checks (MLA_VERIFY_DEBUG; include/mla_verify.h)
+DEBUG_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla_verify_debug.so")
+DEBUG_SLOT_OUT_OF_RANGE = 1
+DEBUG_NEGATIVE_LENGTH = 2
+DEBUG_Q_LEN_OUT_OF_RANGE = 4
 
 MLA_OK = 0
 MLA_ERR_INVALID_ARGUMENT = -1
@@ -57,11 +62,12 @@ SIGNATURES = {
                                                   ctypes.c_int64, _P, _P, _P, _P]),
     "mla_verify_workspace": (ctypes.c_int, [_P, ctypes.POINTER(_P), ctypes.POINTER(ctypes.c_int64),
                                             ctypes.POINTER(_P), ctypes.POINTER(ctypes.c_int64)]),
+    "mla_verify_debug_flags": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_int32), _I32]),
     "mla_verify_destroy": (ctypes.c_int, [_P]),
     "mla_verify_error_string": (ctypes.c_char_p, [ctypes.c_int]),
 }
 
-_lib = None
+_libs = {}
 
 
 class MlaVerifyError(RuntimeError):
@@ -70,22 +76,22 @@ class MlaVerifyError(RuntimeError):
         self.status = status
 
 
-def load() -> ctypes.CDLL:
-    """Load the library once.  Import torch before calling this on a GPU so that
-    the library binds to the HIP runtime torch already loaded."""
-    global _lib
-    if _lib is None:
-        if not os.path.exists(LIB_PATH):
+def load(debug: bool = False) -> ctypes.CDLL:
+    """Load the library once (the debug build with debug=True).  Import torch before calling this
+    on a GPU so that the library binds to the HIP runtime torch already loaded."""
+    path = DEBUG_LIB_PATH if debug else LIB_PATH
+    if path not in _libs:
+        if not os.path.exists(path):
             raise ImportError(
-                f"{LIB_PATH} is not built; run `python -m speculative_decode_mla_amd.build` "
+                f"{path} is not built; run `python -m speculative_decode_mla_amd.build` "
                 "(there is no fallback implementation)")
-        lib = ctypes.CDLL(LIB_PATH)
+        lib = ctypes.CDLL(path)
         for name, (res, args) in SIGNATURES.items():
             fn = getattr(lib, name)
             fn.restype = res
             fn.argtypes = args
-        _lib = lib
-    return _lib
+        _libs[path] = lib
+    return _libs[path]
 
 
 def error_string(status: int) -> str:

@@ -48,12 +48,15 @@ class MlaVerify:
     `form` picks kernel 1's layout (FORM_AUTO, FORM_128ROW or FORM_TWO_STREAM from
     _lib); the result is the same up to rounding, only the speed differs.
     `batch_invariant` makes each request's result bitwise independent of its batchmates
-    (MLA_VERIFY_FLAG_BATCH_INVARIANT: no range plan).
+    (MLA_VERIFY_FLAG_BATCH_INVARIANT: no range plan).  `debug` runs the handle on the debug build
+    of the library, whose kernels clamp out-of-range slots and lengths and record them
+    (debug_flags()).
     """
 
     def __init__(self, num_heads: int, batch: int, max_q_len: int, max_nsplit: int, num_slots: int,
-                 sm_scale: float = DEFAULT_SCALE, form: int = _lib.FORM_AUTO, batch_invariant: bool = False):
-        lib = _lib.load()
+                 sm_scale: float = DEFAULT_SCALE, form: int = _lib.FORM_AUTO, batch_invariant: bool = False,
+                 debug: bool = False):
+        lib = self._lib = _lib.load(debug)
         flags = _lib.FLAG_BATCH_INVARIANT if batch_invariant else 0
         self.cfg = _lib.MlaVerifyConfig(num_heads, D_QK, D_V, batch, max_q_len, max_nsplit, num_slots, sm_scale,
                                         form, flags)
@@ -65,7 +68,7 @@ class MlaVerify:
 
     def close(self):
         if getattr(self, "_h", None) is not None and self._h.value is not None:
-            _lib.check("mla_verify_destroy", _lib.load().mla_verify_destroy(self._h))
+            _lib.check("mla_verify_destroy", self._lib.mla_verify_destroy(self._h))
             self._h = None
 
     def __del__(self):
@@ -74,12 +77,18 @@ class MlaVerify:
         except Exception:
             pass
 
+    def debug_flags(self, clear: bool = True) -> int:
+        """The debug build's flag word (MLA_VERIFY_DEBUG_* bits) after a device synchronisation."""
+        v = ctypes.c_int32()
+        _lib.check("mla_verify_debug_flags", self._lib.mla_verify_debug_flags(self._h, ctypes.byref(v), int(clear)))
+        return v.value
+
     def workspace(self):
         """(o_part pointer, its bytes, lse_part pointer, its bytes) of the handle's split workspace
         (device memory the library owns; see mla_verify_workspace)."""
         op, lp = ctypes.c_void_p(), ctypes.c_void_p()
         ob, lb = ctypes.c_int64(), ctypes.c_int64()
-        _lib.check("mla_verify_workspace", _lib.load().mla_verify_workspace(
+        _lib.check("mla_verify_workspace", self._lib.mla_verify_workspace(
             self._h, ctypes.byref(op), ctypes.byref(ob), ctypes.byref(lp), ctypes.byref(lb)))
         return op.value, ob.value, lp.value, lb.value
 
@@ -100,7 +109,7 @@ class MlaVerify:
     def partials(self, q, kv_pool, slot_idx, seq_lens, q_lens, nsplit: int, stream=None):
         """Kernel 1 only: split partials into the handle's workspace."""
         self._check_inputs(q, kv_pool, slot_idx, seq_lens, q_lens)
-        st = _lib.load().mla_verify_partials(self._h, _ptr(q), _ptr(kv_pool), _ptr(slot_idx), _ptr(seq_lens),
+        st = self._lib.mla_verify_partials(self._h, _ptr(q), _ptr(kv_pool), _ptr(slot_idx), _ptr(seq_lens),
                                              _ptr(q_lens), int(nsplit), _stream_handle(stream))
         _lib.check("mla_verify_partials", st)
 
@@ -124,7 +133,7 @@ class MlaVerify:
             raise ValueError(f"out must be [{q.shape[0]}, {H}, {D_V}], got {tuple(out.shape)}")
         if lse.shape != (q.shape[0], H):
             raise ValueError(f"lse must be [{q.shape[0]}, {H}], got {tuple(lse.shape)}")
-        st = _lib.load().mla_verify_run(self._h, _ptr(q), _ptr(kv_pool), _ptr(slot_idx), _ptr(seq_lens), _ptr(q_lens),
+        st = self._lib.mla_verify_run(self._h, _ptr(q), _ptr(kv_pool), _ptr(slot_idx), _ptr(seq_lens), _ptr(q_lens),
                                         _ptr(out), _ptr(lse), int(nsplit), _stream_handle(stream))
         _lib.check("mla_verify_run", st)
         return out, lse

@@ -12,6 +12,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libmla_verify.so")
+# the same sources with the device-side argument checks compiled in (MLA_VERIFY_DEBUG)
+DEBUG_LIB = os.path.join(HERE, "libmla_verify_debug.so")
 SOURCES = [os.path.join(HERE, "csrc", f) for f in ("mla_verify_api.hip", "mla_verify_kernels.hip", "mla_kv_compact.hip", "mla_step_metadata.hip")]
 ARCH = "gfx950"
 
@@ -41,9 +43,15 @@ def device_asm(source: str, out_path: str) -> str:
 
 
 def build(verbose: bool = False) -> str:
-    """Compile the library; returns its path.  Always recompiles."""
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *COMMON_FLAGS, "-fPIC", "-shared", *SOURCES, "-o", tmp]
+    """Compile the release and the debug library; returns the release library's path.  Always recompiles."""
+    _build_one(LIB, [], verbose)
+    _build_one(DEBUG_LIB, ["-DMLA_VERIFY_DEBUG"], verbose)
+    return LIB
+
+
+def _build_one(path: str, defines, verbose: bool) -> str:
+    tmp = path + ".tmp"
+    cmd = [hipcc(), *COMMON_FLAGS, *defines, "-fPIC", "-shared", *SOURCES, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -53,8 +61,8 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({r.returncode}):\n{msg}")
     if verbose and msg.strip():
         print(msg)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, path)
+    return path
 
 
 if __name__ == "__main__":

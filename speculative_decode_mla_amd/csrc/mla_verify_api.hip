@@ -21,6 +21,7 @@ struct mla_verify_s {
   int32_t workers;      // range plan: workers, one workgroup per row group each (CUs / row groups)
   uint16_t* o_part;  // bf16 [B, max_nsplit, rows_pad, 512]
   float* lse_part;  // [B, max_nsplit, rows_pad]
+  int32_t* debug_flags;  // MLA_VERIFY_DEBUG builds: the device word of mla_verify_debug_flags (else null)
 };
 
 namespace {
@@ -99,6 +100,7 @@ void fill_geometry(const mla_verify_config* cfg, int dev, int cus, mla_verify_s*
   h->workers = h->plan_ranges ? (int32_t)(workers >= 8 ? workers & ~int64_t(7) : workers) : 0;
   h->o_part = nullptr;
   h->lse_part = nullptr;
+  h->debug_flags = nullptr;
 }
 
 // The current device and its CU count.
@@ -140,6 +142,10 @@ int mla_verify_create(const mla_verify_config* cfg, mla_verify_handle* out) {
   if (h == nullptr) return MLA_ERR_OUT_OF_MEMORY;
   st = hip_status(hipMalloc((void**)&h->o_part, (size_t)partial_rows * mlav::kDv * sizeof(uint16_t)));
   if (st == MLA_OK) st = hip_status(hipMalloc((void**)&h->lse_part, (size_t)partial_rows * sizeof(float)));
+#ifdef MLA_VERIFY_DEBUG
+  if (st == MLA_OK) st = hip_status(hipMalloc((void**)&h->debug_flags, sizeof(int32_t)));
+  if (st == MLA_OK) st = hip_status(hipMemset(h->debug_flags, 0, sizeof(int32_t)));
+#endif
   if (st != MLA_OK) {
     (void)hipGetLastError();
     mla_verify_destroy(h);
@@ -199,6 +205,8 @@ int launch_partials(mla_verify_handle h, const void* q, const void* kv_pool, con
   pa.plan_ranges = h->plan_ranges;
   pa.workers = h->workers;
   pa.scale_log2 = c.sm_scale * 1.4426950408889634f;
+  pa.num_slots = c.num_slots;
+  pa.debug_flags = h->debug_flags;
   return mlav::launch_partial(pa, s) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
@@ -270,6 +278,7 @@ int enqueue_run(mla_verify_handle h, const void* q, const void* kv_pool, const i
   ma.part_fp32 = 0;
   ma.plan_ranges = h->plan_ranges;
   ma.workers = h->workers;
+  ma.debug_flags = h->debug_flags;
   return mlav::launch_merge(ma, s) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
@@ -344,6 +353,7 @@ int mla_verify_merge(const float* o_part, const float* lse_part, const int32_t* 
   ma.part_fp32 = 1;
   ma.plan_ranges = 0;
   ma.workers = 0;
+  ma.debug_flags = nullptr;
   return hip_status(mlav::launch_merge(ma, static_cast<hipStream_t>(stream))) == MLA_OK ? MLA_OK : MLA_ERR_HIP;
 }
 
@@ -410,11 +420,26 @@ int mla_verify_workspace(mla_verify_handle h, void** o_part, int64_t* o_part_byt
   return MLA_OK;
 }
 
+int mla_verify_debug_flags(mla_verify_handle h, int32_t* flags, int32_t clear) {
+  if (h == nullptr || flags == nullptr) return MLA_ERR_INVALID_ARGUMENT;
+  *flags = 0;
+#ifdef MLA_VERIFY_DEBUG
+  if (hipDeviceSynchronize() != hipSuccess) return MLA_ERR_HIP;
+  if (hipMemcpy(flags, h->debug_flags, sizeof(int32_t), hipMemcpyDeviceToHost) != hipSuccess) return MLA_ERR_HIP;
+  if (clear != 0 && hipMemset(h->debug_flags, 0, sizeof(int32_t)) != hipSuccess) return MLA_ERR_HIP;
+  return hipDeviceSynchronize() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+#else
+  (void)clear;
+  return MLA_ERR_UNSUPPORTED;
+#endif
+}
+
 int mla_verify_destroy(mla_verify_handle h) {
   if (h == nullptr) return MLA_OK;
   int st = MLA_OK;
   if (h->o_part != nullptr && hipFree(h->o_part) != hipSuccess) st = MLA_ERR_HIP;
   if (h->lse_part != nullptr && hipFree(h->lse_part) != hipSuccess) st = MLA_ERR_HIP;
+  if (h->debug_flags != nullptr && hipFree(h->debug_flags) != hipSuccess) st = MLA_ERR_HIP;
   delete h;
   return st;
 }

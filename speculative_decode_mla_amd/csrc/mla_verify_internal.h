@@ -34,6 +34,8 @@ struct PartialArgs {
   int32_t plan_ranges;       // 1: range plan (128-row form, 2..kRangeMaxBatch requests); 0: splits per request
   int32_t workers;           // range plan: workers (each one workgroup per row group)
   float scale_log2;          // sm_scale * log2(e)
+  int64_t num_slots;         // rows of kv; read only by the MLA_VERIFY_DEBUG build's slot check
+  int32_t* debug_flags;      // MLA_VERIFY_DEBUG builds: device word the checks OR their bits into (or null)
 };
 
 // Kernel 2: one wave per (request, row); merges the row's split partials.
@@ -49,7 +51,13 @@ struct MergeArgs {
   int32_t part_fp32;         // 1: o_part holds fp32 values; 0: bf16
   int32_t plan_ranges;       // 1: kernel 1 ran the range plan with `workers` workers (partials per request from it)
   int32_t workers;
+  int32_t* debug_flags;      // as in PartialArgs
 };
+
+// Bits of the MLA_VERIFY_DEBUG build's device flag word (include/mla_verify.h, mla_verify_debug_flags).
+constexpr int32_t kDebugSlotOutOfRange = 1;
+constexpr int32_t kDebugNegativeLength = 2;
+constexpr int32_t kDebugQLenOutOfRange = 4;
 
 // KV compaction: dst[dst_first + j] = src[slot_idx[j]] (whole 1152-B rows), j < n_rows.
 constexpr int kCompactThreads = 256;

@@ -80,12 +80,55 @@ __device__ __forceinline__ int split_count(int L, int nsplit, int min_tiles) {
   return ns < nsplit ? ns : nsplit;
 }
 
-// q_lens[b] clamped to [0, min(L, max_q_len)] (to [0, max_q_len] when seq_lens is null).
-__device__ __forceinline__ int clamped_q(const int32_t* q_lens, const int32_t* seq_lens, int b, int max_q) {
-  int q = q_lens[b];
-  int lim = (seq_lens != nullptr && seq_lens[b] < max_q) ? seq_lens[b] : max_q;
-  q = q < lim ? q : lim;
-  return q > 0 ? q : 0;
+// Checks of device-visible arguments, compiled in only for the MLA_VERIFY_DEBUG build: a bad value
+// is replaced before it is used for any access, and the check ORs its bit into *flags.  In the
+// release build every one of them is the identity.
+__device__ __forceinline__ void debug_flag(int32_t* flags, int32_t bit) {
+#ifdef MLA_VERIFY_DEBUG
+  if (flags != nullptr) atomicOr(flags, bit);
+#else
+  (void)flags;
+  (void)bit;
+#endif
+}
+
+// seq_lens[b]; the debug build reads a negative length as 0.
+__device__ __forceinline__ int read_len(const int32_t* seq_lens, int b, int32_t* flags) {
+  int L = seq_lens[b];
+#ifdef MLA_VERIFY_DEBUG
+  if (L < 0) {
+    debug_flag(flags, kDebugNegativeLength);
+    L = 0;
+  }
+#endif
+  (void)flags;
+  return L;
+}
+
+// A slot index read from slot_idx; the debug build clamps it into [0, num_slots).
+__device__ __forceinline__ int checked_slot(int slot, int64_t num_slots, int32_t* flags) {
+#ifdef MLA_VERIFY_DEBUG
+  if (slot < 0 || (int64_t)slot >= num_slots) {
+    debug_flag(flags, kDebugSlotOutOfRange);
+    slot = slot < 0 ? 0 : (int)(num_slots - 1);
+  }
+#endif
+  (void)num_slots;
+  (void)flags;
+  return slot;
+}
+
+// q_lens[b] clamped to [0, min(L, max_q_len)] (to [0, max_q_len] when seq_lens is null); the debug
+// build also flags a value it had to clamp.
+__device__ __forceinline__ int clamped_q(const int32_t* q_lens, const int32_t* seq_lens, int b, int max_q,
+                                         int32_t* flags = nullptr) {
+  const int q0 = q_lens[b];
+  const int L = seq_lens != nullptr ? read_len(seq_lens, b, flags) : max_q;
+  const int lim = L < max_q ? L : max_q;
+  int q = q0 < lim ? q0 : lim;
+  q = q > 0 ? q : 0;
+  if (q != q0 && seq_lens != nullptr) debug_flag(flags, kDebugQLenOutOfRange);
+  return q;
 }
 
 __device__ __forceinline__ float wave_max(float v) {
@@ -268,8 +311,8 @@ __device__ __forceinline__ bool decode_work(const PartialArgs& p, int wg, int ro
   }
   wi.b = wi.bs / p.nsplit;
   wi.s = wi.bs - wi.b * p.nsplit;
-  wi.L = p.seq_lens[wi.b];
-  wi.Q = clamped_q(p.q_lens, p.seq_lens, wi.b, p.max_q_len);
+  wi.L = read_len(p.seq_lens, wi.b, p.debug_flags);
+  wi.Q = clamped_q(p.q_lens, p.seq_lens, wi.b, p.max_q_len, p.debug_flags);
   wi.R = wi.Q * p.heads;
   if (wi.Q <= 0 || wi.g * rows_per_group >= wi.R) return false;
   const int ns = split_count(wi.L, p.nsplit, p.min_tiles);
@@ -279,8 +322,8 @@ __device__ __forceinline__ bool decode_work(const PartialArgs& p, int wg, int ro
   wi.t_end = (int)((int64_t)(wi.s + 1) * tiles / ns);
   int64_t ko = 0, qo = 0;
   for (int i = 0; i < wi.b; ++i) {
-    ko += p.seq_lens[i];
-    qo += clamped_q(p.q_lens, p.seq_lens, i, p.max_q_len);
+    ko += read_len(p.seq_lens, i, p.debug_flags);
+    qo += clamped_q(p.q_lens, p.seq_lens, i, p.max_q_len, p.debug_flags);
   }
   wi.ko = ko;
   wi.qo = qo;
@@ -325,11 +368,11 @@ __device__ __forceinline__ int wave_excl_scan(int v, int lane) {
 }
 
 __device__ __forceinline__ RequestScan scan_requests(const int32_t* seq_lens, const int32_t* q_lens, int batch,
-                                                     int max_q) {
+                                                     int max_q, int32_t* flags) {
   const int lane = threadIdx.x & 63;
   RequestScan r;
-  r.L = lane < batch ? seq_lens[lane] : 0;
-  r.Q = lane < batch ? clamped_q(q_lens, seq_lens, lane, max_q) : 0;
+  r.L = lane < batch ? read_len(seq_lens, lane, flags) : 0;
+  r.Q = lane < batch ? clamped_q(q_lens, seq_lens, lane, max_q, flags) : 0;
   r.tiles = r.Q > 0 ? (r.L + kTileKeys - 1) / kTileKeys : 0;
   r.J = wave_excl_scan(r.tiles, lane);
   r.qo = wave_excl_scan(r.Q, lane);
@@ -387,7 +430,7 @@ __host__ __device__ __forceinline__ int64_t range_grid(int workers, int row_grou
 // Decode a workgroup id of the range plan; false if it has nothing to do.
 __device__ __forceinline__ bool decode_piece(const PartialArgs& p, int wg, WorkItem& wi) {
   const int lane = threadIdx.x & 63;
-  const RequestScan r = scan_requests(p.seq_lens, p.q_lens, p.batch, p.max_q_len);
+  const RequestScan r = scan_requests(p.seq_lens, p.q_lens, p.batch, p.max_q_len, p.debug_flags);
   const int C = __builtin_amdgcn_readfirstlane(range_chunk(r, p.nsplit, p.workers, p.min_tiles));
   const int T = __builtin_amdgcn_readlane(r.J + r.tiles, 63);
   const int pools = range_pools(p.workers), per_pool = p.workers / pools;
@@ -475,7 +518,7 @@ __device__ __forceinline__ void redo_rows_exact(const PartialArgs& p, const Work
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int key = (wi.t_begin + tile_first) * kTileKeys; key < kend;
          key += (key + 1) % kTileKeys == 0 ? 1 + (tile_step - 1) * kTileKeys : 1) {  // skip the other stream's tiles
-      const uint16_t* krow = p.kv + (int64_t)slots[key] * kDqk;
+      const uint16_t* krow = p.kv + (int64_t)checked_slot(slots[key], p.num_slots, p.debug_flags) * kDqk;
       float dot = 0.f;
 #pragma unroll
       for (int d = 0; d < 9; ++d) dot += qv[d] * bf16f(krow[d * 64 + lane]);
@@ -649,6 +692,8 @@ __device__ __forceinline__ void partial_item(const PartialArgs& p, const WorkIte
   }
   // slot indices and q rows have landed; the memory clobber keeps the LDS reads below after it
   asm volatile("s_waitcnt vmcnt(0)" : "+v"(sl[0]), "+v"(sl[1]), "+v"(sl[2]) : : "memory");
+#pragma unroll
+  for (int i = 0; i < kAhead; ++i) sl[i] = checked_slot(sl[i], p.num_slots, p.debug_flags);
   bf16x8 qf[kQkSteps];
   {
     const lds_char* qb = smem + w * kTileBytes;
@@ -766,7 +811,7 @@ __device__ __forceinline__ void partial_item(const PartialArgs& p, const WorkIte
     const int key0 = t * kTileKeys + 4 * hi;
     // Slot of the row this lane gathers for tile i+3, loaded now and awaited with the tile
     // loads before the barrier below.
-    const int g_slot = kRefill ? slots_g[gather_key(i + kAhead)] : 0;
+    const int g_slot = kRefill ? checked_slot(slots_g[gather_key(i + kAhead)], p.num_slots, p.debug_flags) : 0;
     // (no drain: the last MFMA that wrote sacc is a whole P.V phase back)
     SoftmaxTile sm;
     if (t * kTileKeys + kTileKeys > mask_from) mask_tile(sacc, key0, limit);
@@ -1038,6 +1083,8 @@ void mla_verify_partial_2s(PartialArgs p) {
   }
   // the slot indices have landed (the 36 q loads issued after them may still be in flight)
   asm volatile("s_waitcnt vmcnt(36)" : "+v"(sl[0]), "+v"(sl[1]) : : "memory");
+#pragma unroll
+  for (int j = 0; j < 2; ++j) sl[j] = checked_slot(sl[j], p.num_slots, p.debug_flags);
   if (nst > 0) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) dma_key_block(g_row(sl[j], j), g_lds(0, j));
@@ -1103,8 +1150,8 @@ void mla_verify_partial_2s(PartialArgs p) {
     MLAV_WAIT_VMCNT(0);  // this stream's tile k (and the slot loads for the next gather) have landed
     __syncthreads();     // every stream's tile k is visible; every wave is done with step k-1
     const bool refill = k + 1 < nst;
-    const char* r0 = g_row(sn[0], 0);
-    const char* r1 = g_row(sn[1], 1);
+    const char* r0 = g_row(checked_slot(sn[0], p.num_slots, p.debug_flags), 0);
+    const char* r1 = g_row(checked_slot(sn[1], p.num_slots, p.debug_flags), 1);
     if (refill) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) sn[j] = slots_g[gather_key(k + 2, j)];
@@ -1330,17 +1377,17 @@ __global__ __launch_bounds__(64 * kMergeGroups * kRowsPerBlock) void mla_verify_
   int ns;
   int64_t qo = 0;
   if (p.plan_ranges) {
-    const RequestScan rq = scan_requests(p.seq_lens, p.q_lens, p.batch, p.max_q_len);
+    const RequestScan rq = scan_requests(p.seq_lens, p.q_lens, p.batch, p.max_q_len, p.debug_flags);
     if (r >= __builtin_amdgcn_readlane(rq.Q, b) * p.heads) return;
     const int C = range_chunk(rq, p.nsplit, p.workers, p.min_tiles);
     const int J = __builtin_amdgcn_readlane(rq.J, b), tiles = __builtin_amdgcn_readlane(rq.tiles, b);
     ns = (J + tiles - 1) / C - J / C + 1;  // (tiles > 0: the request has rows)
     qo = __builtin_amdgcn_readlane(rq.qo, b);
   } else {
-    const int Q = clamped_q(p.q_lens, p.seq_lens, b, p.max_q_len);
+    const int Q = clamped_q(p.q_lens, p.seq_lens, b, p.max_q_len, p.debug_flags);
     if (r >= Q * p.heads) return;
-    ns = p.use_all_splits ? p.nsplit : split_count(p.seq_lens[b], p.nsplit, p.min_tiles);
-    for (int i = 0; i < b; ++i) qo += clamped_q(p.q_lens, p.seq_lens, i, p.max_q_len);
+    ns = p.use_all_splits ? p.nsplit : split_count(read_len(p.seq_lens, b, p.debug_flags), p.nsplit, p.min_tiles);
+    for (int i = 0; i < b; ++i) qo += clamped_q(p.q_lens, p.seq_lens, i, p.max_q_len, p.debug_flags);
   }
 
   const int64_t base = (int64_t)b * p.nsplit * p.rows_stride + r;  // (b, s=0, r)
@@ -1442,11 +1489,11 @@ __global__ __launch_bounds__(256) void mla_verify_merge_sliced(MergeArgs p) {
   const int b = (int)(row_id / rows_per_b);
   const int r = (int)(row_id - (int64_t)b * rows_per_b);
   if (b >= p.batch) return;
-  const int Q = clamped_q(p.q_lens, p.seq_lens, b, p.max_q_len);
+  const int Q = clamped_q(p.q_lens, p.seq_lens, b, p.max_q_len, p.debug_flags);
   if (r >= Q * p.heads) return;  // uniform over the workgroup
-  const int ns = p.use_all_splits ? p.nsplit : split_count(p.seq_lens[b], p.nsplit, p.min_tiles);
+  const int ns = p.use_all_splits ? p.nsplit : split_count(read_len(p.seq_lens, b, p.debug_flags), p.nsplit, p.min_tiles);
   int64_t qo = 0;
-  for (int i = 0; i < b; ++i) qo += clamped_q(p.q_lens, p.seq_lens, i, p.max_q_len);
+  for (int i = 0; i < b; ++i) qo += clamped_q(p.q_lens, p.seq_lens, i, p.max_q_len, p.debug_flags);
 
   const int64_t base = (int64_t)b * p.nsplit * p.rows_stride + r;  // (b, s=0, r)
   const float* lse_s = p.lse_part + base;

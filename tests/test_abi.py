@@ -26,18 +26,30 @@ def lib():
 
 def test_header_declares_the_boundary():
     assert _declared() == ["mla_verify_build_metadata", "mla_verify_compact", "mla_verify_create",
-                           "mla_verify_destroy", "mla_verify_error_string", "mla_verify_merge",
-                           "mla_verify_partials", "mla_verify_run", "mla_verify_run_noalloc",
+                           "mla_verify_debug_flags", "mla_verify_destroy", "mla_verify_error_string",
+                           "mla_verify_merge", "mla_verify_partials", "mla_verify_run", "mla_verify_run_noalloc",
                            "mla_verify_workspace"]
 
 
-def test_every_declared_symbol_is_exported(lib):
-    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
+@pytest.mark.parametrize("debug", [False, True], ids=["release", "debug build"])
+def test_every_declared_symbol_is_exported(lib, debug):
+    path = _lib.DEBUG_LIB_PATH if debug else _lib.LIB_PATH
+    if not os.path.exists(path):
+        pytest.skip("library not built")
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True).stdout
     exported = set(re.findall(r" T (mla_verify_\w+)$", out, re.M))
-    assert set(_declared()) <= exported
+    assert set(_declared()) == exported  # and nothing else under the library's prefix
     assert set(_declared()) == set(_lib.SIGNATURES)
+    dl = _lib.load(debug)
     for name in _declared():
-        assert hasattr(lib, name)
+        assert hasattr(dl, name)
+
+
+def test_debug_flags_host_checks(lib):
+    flags = ctypes.c_int32(7)
+    assert lib.mla_verify_debug_flags(None, ctypes.byref(flags), 0) == _lib.MLA_ERR_INVALID_ARGUMENT
+    if os.path.exists(_lib.DEBUG_LIB_PATH):
+        assert _lib.load(True).mla_verify_debug_flags(None, ctypes.byref(flags), 0) == _lib.MLA_ERR_INVALID_ARGUMENT
 
 
 def test_config_struct_layout_matches_header():
