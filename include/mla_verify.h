@@ -160,7 +160,11 @@ int mla_verify_run_noalloc(const mla_verify_config* cfg, const void* q, const vo
 
 /*
  * Kernel 1 alone: the split partials of one call, left in the handle's
- * workspace (the "partial" half of the pages' partial + reduce).  Arguments
+ * workspace: the partial half of the KV-split partial + reduce scheme (magik.net,
+ * "The Decisive A/B", sections "The Context: A Custom Kernel in Production" and
+ * "What This Reveals About the Bottleneck").  Partial s of a row is that row's
+ * softmax attention over the s-th chunk of its keys, normalised within the chunk,
+ * with the chunk's natural-log LSE.  Arguments
  * as in mla_verify_run.  mla_verify_run is this call followed by the merge;
  * this entry exists to time and inspect the partial phase by itself.
  */
@@ -168,8 +172,11 @@ int mla_verify_partials(mla_verify_handle h, const void* q, const void* kv_pool,
                         const int32_t* seq_lens, const int32_t* q_lens, int32_t nsplit, void* stream);
 
 /*
- * Kernel 2 alone: merge caller-provided split partials (the reduce of the
- * pages' partial + reduce scheme).  Every one of the nsplit partials of a row
+ * Kernel 2 alone: merge caller-provided split partials, the reduce half of the
+ * KV-split partial + reduce scheme (magik.net, "The Decisive A/B", sections "The
+ * Context: A Custom Kernel in Production" and "Input and Output Knowledge"):
+ *     lse = log sum_s exp(lse_s),   out = sum_s exp(lse_s - lse) * o_s,
+ * -inf partials skipped.  Every one of the nsplit partials of a row
  * takes part; a partial with lse = -inf carries no weight.
  *   o_part   device fp32 [batch, nsplit, max_q_len * H, 512]: partial outputs,
  *            each already normalised within its chunk; row r of request b is
