@@ -544,16 +544,25 @@ __device__ __forceinline__ void redo_rows_exact(const PartialArgs& p, const Work
 // Per-row softmax state of one lane (row lrow; the lane pair l, l^32 agrees on
 // m_ref and holds half of each row sum).
 struct RowSoftmax {
-  float m_ref;    // reference max (log2 units): the row max of the split's first tile; -inf if none is visible
+  float m_ref;    // reference (log2 units): the row max of the split's first tile + kRefHeadroom; -inf if none is visible
   float l_run;    // this lane's share of the row sum of bf16-rounded P (normalises O)
   float l_exact;  // ... and of P before rounding (gives the LSE)
 };
 
-// p = 2^(x - m_ref) is used as is, with no rescale, as long as the row sums stay
-// below 2^64: then every p is below 2^64 and, over at most 2^31 keys, neither
-// the sums nor the output accumulators can overflow fp32.  A row whose sum
-// reaches it (including +inf from an overflowing exp2) is redone exactly.
-constexpr float kRowSumLimit = 18446744073709551616.0f;  // 2^64
+// p = 2^(x - m_ref) is used as is, with no rescale, as long as the row sums stay below 2^96:
+// then every p is below 2^96 and, over at most 2^31 keys, neither the sums nor the output
+// accumulators (|v| < 2^31) can overflow fp32.  A row whose sum reaches it (including +inf from
+// an overflowing exp2) is redone exactly.
+//
+// The reference sits kRefHeadroom = 64 binades above the first tile's row max.  fp32 and bf16
+// keep their relative precision from 2^-126 up, so scaling every p (and both row sums) by
+// exactly 2^-64 changes no rounding, while a key may now score up to about 64 + 96 - log2(keys
+// in the split) binades above the first tile's max (about 100 nats at 2,048 keys) before the
+// sums reach the limit, instead of 64 - log2(keys).  The price is at the bottom: a p below
+// 2^-126 is flushed, i.e. a key more than 62 binades below the first tile's max, whose weight
+// next to that max key (which is in the same sum) is below 2^-62 -- far under fp32 precision.
+constexpr float kRowSumLimit = 79228162514264337593543950336.0f;  // 2^96
+constexpr float kRefHeadroom = 64.0f;
 
 // Row max of a tile's raw scores: 16 values per lane, then the lane pair.
 __device__ __forceinline__ float tile_row_max(const f32x16& s) {
@@ -734,7 +743,7 @@ __device__ __forceinline__ void partial_item(const PartialArgs& p, const WorkIte
     o_par[c] = (f32x16){};
   }
   // Softmax with a fixed per-row reference: m_ref is the row max of the split's
-  // first tile (set after its Q.K below); p = 2^(x - m_ref) needs no rescale
+  // first tile plus kRefHeadroom (set after its Q.K below); p = 2^(x - m_ref) needs no rescale
   // while the row sum stays below kRowSumLimit.  A row that reaches it is
   // recomputed exactly at the end (redo_rows_exact).
   RowSoftmax st{-INFINITY, 0.f, 0.f};
@@ -779,7 +788,8 @@ __device__ __forceinline__ void partial_item(const PartialArgs& p, const WorkIte
     asm volatile(MLAV_MFMA_DRAIN : "+v"(sacc));
     f32x16 s0 = sacc;
     if (wi.t_begin * kTileKeys + kTileKeys > mask_from) mask_tile(s0, wi.t_begin * kTileKeys + 4 * hi, limit);
-    st.m_ref = tile_row_max(s0) * p.scale_log2;  // the scale is positive, so it commutes with the max
+    // (the scale is positive, so it commutes with the max; -inf stays -inf)
+    st.m_ref = tile_row_max(s0) * p.scale_log2 + kRefHeadroom;
     nmref = (st.m_ref == -INFINITY) ? 0.f : -st.m_ref;
   }
   if (ntiles > 1) {
@@ -902,7 +912,7 @@ __device__ __forceinline__ void partial_item(const PartialArgs& p, const WorkIte
   // whether any row of the workgroup needs the exact redo.
   const float lt = pair_sum(st.l_run);
   const float le = pair_sum(st.l_exact);
-  const bool overflow = !(le < kRowSumLimit);  // some p reached 2^64, or an exp2 overflowed to +inf
+  const bool overflow = !(le < kRowSumLimit);  // the row sum reached 2^96, or an exp2 overflowed to +inf
   const uint64_t redo = __ballot(overflow && hi == 0 && row_valid);
   __syncthreads();  // every wave is done with the ring and the P exchange buffers
   float* lsum = (float*)(smem_raw + kRing * kTileBytes);
@@ -1183,7 +1193,7 @@ void mla_verify_partial_2s(PartialArgs p) {
       const int t = wi.t_begin + 2 * k + stream;
       if (t * kTileKeys + kTileKeys > mask_from) mask_tile(sacc, t * kTileKeys + 4 * hi, limit);
       if (k == 0) {  // the stream's reference: the row max of its first tile (see the 128-row form)
-        st.m_ref = tile_row_max(sacc) * p.scale_log2;
+        st.m_ref = tile_row_max(sacc) * p.scale_log2 + kRefHeadroom;
         nmref = (st.m_ref == -INFINITY) ? 0.f : -st.m_ref;
       }
       scale_scores(sm, sacc, nmref, p.scale_log2);

@@ -14,6 +14,7 @@ dims followed by 64 rope dims, and v is the first 512 dims):
   ctx64k    B=1,  H=64, Q=16, L=65536, 2M-slot pool,    nsplit=32
   ctx91k    B=1,  H=64, Q=16, L=91000, 2M-slot pool,    nsplit=32
   batch16   B=16, H=64, Q=16, L_b log-uniform in [1k, 64k], 4M-slot pool, nsplit=32
+  ctx64k_sink  ctx64k's inputs, then one planted dominant key in every 2,048-key chunk (below)
 
 Draw order for a seed (fixed, so that every consumer sees the same bytes):
   1. rng = numpy.random.default_rng(seed)
@@ -21,6 +22,12 @@ Draw order for a seed (fixed, so that every consumer sees the same bytes):
   3. slots = rng.permutation(num_slots)[:sum(L)]; request b takes the next L_b
   4. kv rows = standard_normal((sum(L), 576), float32) -> bf16 (RNE)
   5. q = standard_normal((sum(Q), H, 576), float32) -> bf16 (RNE)
+  6. planted keys (workloads with sink_nats > 0 only, after all of the above, so the
+     other draws are those of the plain workload): in every chunk of sink_every keys of
+     request 0, key chunk_start + 32 + integers(0, sink_every - 32) (never in the chunk's
+     first 32 keys) becomes bf16(c * q[t, h]) for a random (token, head) row (t, h), with
+     c = sink_nats / (scale * |q[t, h]|^2): that row's score for the key is about sink_nats
+     nats, far above the scores of N(0, 1) keys (a few nats), like an attention sink.
 Pool rows that no request references hold the bf16 quiet NaN 0x7FC0, so a
 stray read shows up as NaN in the result.
 """
@@ -49,6 +56,8 @@ class Workload:
     seed: int
     ctx_lo: int = 1024
     ctx_hi: int = 65536
+    sink_nats: float = 0.0   # > 0: plant one dominant key per chunk of sink_every keys (draw step 6)
+    sink_every: int = 2048
 
 
 WORKLOADS = {
@@ -60,6 +69,8 @@ WORKLOADS = {
     "batch16": Workload("batch16", 16, 64, 16, None, 1 << 22, 32, 5),
     # q_len = 1 decode steps (one token per request, no drafts to verify)
     "decode64k": Workload("decode64k", 1, 64, 1, 65536, 1 << 21, 256, 6),
+    # ctx64k with one key per 2,048-key chunk (one split each at nsplit 32) scoring ~60 nats for one row
+    "ctx64k_sink": Workload("ctx64k_sink", 1, 64, 16, 65536, 1 << 21, 32, 3, sink_nats=60.0),
     "decode_batch16": Workload("decode_batch16", 16, 64, 1, None, 1 << 22, 32, 7),
 }
 
@@ -128,7 +139,25 @@ def make_inputs(w: Workload | str, seed: int | None = None) -> VerifyInputs:
     else:
         lens = np.full(w.batch, w.ctx, dtype=np.int64)
     qlens = np.full(w.batch, w.q_len, dtype=np.int64)
-    return make_custom(rng, lens, qlens, w.heads, w.num_slots)
+    x = make_custom(rng, lens, qlens, w.heads, w.num_slots)
+    if w.sink_nats > 0:
+        plant_dominant_keys(rng, x, w.sink_nats, w.sink_every)
+    return x
+
+
+def plant_dominant_keys(rng: np.random.Generator, x: VerifyInputs, nats: float, every: int) -> None:
+    """Draw step 6: in every chunk of `every` keys of request 0, one key (not among the chunk's
+    first 32) becomes bf16(c * q[t, h]) for a random row, c = nats / (scale * |q[t, h]|^2)."""
+    L, Q = int(x.seq_lens[0]), int(x.q_lens[0])
+    for start in range(0, L, every):
+        span = min(every, L - start)
+        if span <= 32:
+            break
+        j = start + 32 + int(rng.integers(0, span - 32))
+        t, h = int(rng.integers(0, Q)), int(rng.integers(0, x.heads))
+        qv = (x.q[t, h].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        c = nats / (x.scale * float(np.dot(qv, qv)))
+        x.kv_rows[j] = f32_to_bf16_bits((c * qv).astype(np.float32))
 
 
 def make_custom(rng: np.random.Generator, seq_lens, q_lens, heads: int, num_slots: int,

@@ -96,7 +96,7 @@ def _check_full(api, x, nsplit, label):
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("workload", ["ctx23k", "ctx64k", "ctx91k", "batch16"])
+@pytest.mark.parametrize("workload", ["ctx23k", "ctx64k", "ctx91k", "batch16", "ctx64k_sink"])
 def test_full_size_parity(api, workload):
     """The large workloads at their full sizes and split counts, as the benchmark runs them: every
     (token, head) row of out and lse against the oracle."""
