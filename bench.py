@@ -42,14 +42,15 @@ def algorithmic_counts(x):
     return flops, kv_bytes, alg_bytes
 
 
-def measured_traffic(workload: str):
+def measured_traffic(kernel: str, workload: str):
     """HBM bytes per kernel-1 launch from the committed rocprofv3 counter summary, or None.
 
-    The summary records the sha256 of the kernel source it was taken on; once the
-    source differs, the counters no longer describe the kernel and None is returned.
+    The summary (profiles/<kernel>_<workload>_traffic.md) records the sha256 of the kernel
+    source it was taken on; once the source differs, the counters no longer describe the kernel
+    and None is returned.
     """
     import hashlib
-    path = os.path.join(ROOT, "profiles", f"mla_verify_partial_{workload}_traffic.md")
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.md")
     src = os.path.join(ROOT, "speculative_decode_mla_amd", "csrc", "mla_verify_kernels.hip")
     if not (os.path.exists(path) and os.path.exists(src)):
         return None
@@ -462,7 +463,7 @@ def main():
         roofline = {"bound": "mfma", "kernel": k1_kernel,
                     "achieved": round(k1_tflops, 1) if k1_tflops else None, "peak": PEAK_BF16_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(k1_tflops / PEAK_BF16_TFLOPS, 4) if k1_tflops else None,
-                    "traffic": measured_traffic(w.name), "traffic_unit": "bytes/launch",
+                    "traffic": measured_traffic(k1_kernel, w.name), "traffic_unit": "bytes/launch",
                     "flops_per_launch": flops,
                     "call_achieved": round(call_tflops, 1), "call_frac": round(call_tflops / PEAK_BF16_TFLOPS, 4)}
     else:
@@ -471,7 +472,7 @@ def main():
         roofline = {"bound": "hbm", "kernel": k1_kernel,
                     "achieved": round(k1_gbps, 1) if k1_gbps else None, "peak": PEAK_HBM_GBPS,
                     "unit": "GB/s", "frac": round(k1_gbps / PEAK_HBM_GBPS, 4) if k1_gbps else None,
-                    "traffic": measured_traffic(w.name), "traffic_unit": "bytes/launch",
+                    "traffic": measured_traffic(k1_kernel, w.name), "traffic_unit": "bytes/launch",
                     "bytes_per_launch": alg_bytes,
                     "call_achieved": round(call_gbps, 1), "call_frac": round(call_gbps / PEAK_HBM_GBPS, 4)}
     res = {

@@ -62,7 +62,7 @@ constexpr int kQkSteps = kDqk / 16;                // 36 MFMA k-steps over 576 d
 constexpr int kColBlocks = kDv / 32;               // 16 blocks of 32 output columns
 constexpr int kHalfColBlocks = kColBlocks / 2;     // column blocks of one wave of a pair
 constexpr int kPvFrags = 2 * kHalfColBlocks;       // V^T fragments per wave per tile (2 MFMAs each)
-constexpr int kPrefetch = 6;                       // K fragment reads kept ahead of their MFMA
+constexpr int kPrefetch = 4;                       // K fragment reads kept ahead of their MFMA
 constexpr int kVPrefetch = 4;                      // V^T fragment reads kept ahead
 constexpr int kDmaPerTile = 9;                     // direct-to-LDS loads per wave per tile
 constexpr int kStageRowBytes = 528;                // epilogue: one bf16 row half (512 B) + 16 B of padding
@@ -686,17 +686,17 @@ __device__ __forceinline__ void partial_item(const PartialArgs& p, const WorkIte
   // The wave's 32 query rows, resident in registers for the whole split: lane holds row lrow,
   // dims 16*ks + 8*hi .. +7 (MFMA B-operand layout).  Loads straight into that layout would make
   // every load touch 32 rows (32 partial 128-B lines), which costs microseconds of address
-  // processing per workgroup; so wave w moves its rows into ring buffer w in the key-tile layout
-  // (row r of the wave as key r; 8 whole lines per load) and reads them back with the Q.K read
-  // pattern.  A row past the request reads the request's first row instead: its scores are finite
+  // processing per workgroup; so wave w moves its rows into block w of the ring buffers in the
+  // key-tile layout (row r of the wave as key r of block w of buffer r/8; 8 whole lines per load)
+  // and reads them back with the Q.K read pattern.  A row past the request reads the request's first row instead: its scores are finite
   // and its output is never stored.
   {
-    const uint32_t qbuf = smem_base + w_uniform * kTileBytes;
+    const uint32_t qbuf = smem_base + w_uniform * kKeyBlockBytes;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       const int r = row0 + w * kRowsPerWave + 8 * kb + g_kr;
       const int64_t qrow = wi.qo * H + (r < R ? r : 0);
-      dma_key_block((const char*)(p.q + qrow * kDqk) + (((lane & 7) ^ g_kr ^ (kb & 1)) << 4), qbuf + kb * kKeyBlockBytes);
+      dma_key_block((const char*)(p.q + qrow * kDqk) + (((lane & 7) ^ g_kr ^ (kb & 1)) << 4), qbuf + kb * kTileBytes);
     }
   }
   // slot indices and q rows have landed; the memory clobber keeps the LDS reads below after it
@@ -705,16 +705,17 @@ __device__ __forceinline__ void partial_item(const PartialArgs& p, const WorkIte
   for (int i = 0; i < kAhead; ++i) sl[i] = checked_slot(sl[i], p.num_slots, p.debug_flags);
   bf16x8 qf[kQkSteps];
   {
-    const lds_char* qb = smem + w * kTileBytes;
+    // q row lrow of the wave sits in buffer lrow/8, block w: kaddr's key-block offset replaced
+    const lds_char* qb = smem + w * kKeyBlockBytes + (lrow >> 3) * (kTileBytes - kKeyBlockBytes);
 #pragma unroll
     for (int ks = 0; ks < kQkSteps; ++ks)
       qf[ks] = *(const __attribute__((address_space(3))) bf16x8*)(qb + kaddr[ks & 3] + (ks >> 2) * kBlockBytes);
   }
-  // every wave holds its q before the ring is refilled with tiles; tile 0 first, tiles 1 and 2
-  // between the Q.K MFMAs of tile 0 (each gather load takes the address unit for a while, so
-  // issuing all three here would delay the first Q.K)
+  // Block w of every buffer held this wave's q rows only, so once its own reads are done the wave
+  // gathers its eight keys of tile 0 into block w of buffer 0 without waiting for the other waves;
+  // tiles 1 and 2 go between the Q.K MFMAs of tile 0 (each gather load takes the address unit for
+  // a while, so issuing all three here would delay the first Q.K).
   asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
-  __syncthreads();
   issue_tile(0, sl[0]);
 
   // ---- per-lane LDS read addresses for P.V (relative to a tile buffer) --------------------------
@@ -948,7 +949,8 @@ __device__ __forceinline__ void partial_item(const PartialArgs& p, const WorkIte
     const int r = 2 * k + hi;
     const i32x4 v = *(const __attribute__((address_space(3))) i32x4*)(stage + r * kStageRowBytes + (lane & 31) * 16);
     const int grow = row0 + (r < 32 ? w * kRowsPerWave + r : partner * kRowsPerWave + r - 32);
-    if (grow < R) *(i32x4*)(part_base + (int64_t)grow * kDv) = v;
+    // (nontemporal: the merge reads the partials from another XCD, not from this L2)
+    if (grow < R) __builtin_nontemporal_store(v, (i32x4*)(part_base + (int64_t)grow * kDv));
   };
 #pragma unroll
   for (int c = 0; c < kHalfColBlocks; ++c)
