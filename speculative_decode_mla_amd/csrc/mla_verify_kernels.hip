@@ -934,7 +934,9 @@ __device__ __forceinline__ void partial_item(const PartialArgs& p, const WorkIte
   // per store instruction.  In the C layout the lane holds, per 32-column block c, columns
   // 32c + 8*q4 + 4*hi .. +3.  The wave's own rows (stage rows 0..31) are staged first and
   // stored while its partner's rows (stage rows 32..63) are converted, so the stores drain
-  // under the conversion work.
+  // under the conversion work.  Each half goes out as 16 LDS reads, one wait, then 16 stores:
+  // a read, wait and store per row pair costs an LDS round trip per store (about 2 us a
+  // workgroup).
   typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
   lds_char* stage = smem + w * kStageBytes;
   auto stage_block = [&](const f32x16& o, float inv, int row, int c, int q4) {
@@ -945,26 +947,30 @@ __device__ __forceinline__ void partial_item(const PartialArgs& p, const WorkIte
   };
   // (the column half from the wave index in a scalar register: keeping `half` live this long spilled it)
   uint16_t* part_base = p.o_part + (int64_t)wi.bs * p.rows_pad * kDv + (w_uniform & 1) * (kDv / 2) + (lane & 31) * 8;
-  auto store_pair = [&](int k) {  // stage rows 2k and 2k+1
-    const int r = 2 * k + hi;
-    const i32x4 v = *(const __attribute__((address_space(3))) i32x4*)(stage + r * kStageRowBytes + (lane & 31) * 16);
-    const int grow = row0 + (r < 32 ? w * kRowsPerWave + r : partner * kRowsPerWave + r - 32);
-    // (nontemporal: the merge reads the partials from another XCD, not from this L2)
-    if (grow < R) __builtin_nontemporal_store(v, (i32x4*)(part_base + (int64_t)grow * kDv));
+  auto store_half = [&](const int r0, const int grow0) {  // stage rows r0 .. r0+31 = rows grow0 ..
+    i32x4 v[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+      v[k] = *(const __attribute__((address_space(3))) i32x4*)(stage + (r0 + 2 * k + hi) * kStageRowBytes + (lane & 31) * 16);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int grow = grow0 + 2 * k + hi;
+      // (nontemporal: the merge reads the partials from another XCD, not from this L2)
+      if (grow < R) __builtin_nontemporal_store(v[k], (i32x4*)(part_base + (int64_t)grow * kDv));
+    }
+    __builtin_amdgcn_sched_barrier(0);
   };
 #pragma unroll
   for (int c = 0; c < kHalfColBlocks; ++c)
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) stage_block(o_own[c], inv_own, lrow, c, q4);
+  store_half(0, row0 + w * kRowsPerWave);
 #pragma unroll
   for (int c = 0; c < kHalfColBlocks; ++c)
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      stage_block(o_par[c], inv_par, 32 + lrow, c, q4);
-      if (q4 & 1) store_pair(2 * c + (q4 >> 1));  // own rows: pairs 0..15
-    }
-#pragma unroll
-  for (int k = 16; k < 32; ++k) store_pair(k);  // the partner's rows
+    for (int q4 = 0; q4 < 4; ++q4) stage_block(o_par[c], inv_par, 32 + lrow, c, q4);
+  store_half(32, row0 + partner * kRowsPerWave);
 
   // Rows whose sums outgrew the fixed reference are redone exactly by their owner wave,
   // once both halves of the row have been written.
