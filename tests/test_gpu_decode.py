@@ -1,6 +1,8 @@
 """GPU parity for q_len = 1 decode steps (and other requests of at most 64 rows), which run the
 two-stream form of kernel 1: against the fp64 oracle, max |out err| <= 1e-2, max |lse err| <= 1e-3.
 All calls go through the C ABI."""
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -60,22 +62,32 @@ def test_decode_split_count_does_not_change_result(api):
     assert max(np.max(np.abs(o - outs[0])) for o in outs) <= OUT_TOL
 
 
-def test_decode_overflow_fallback_rows(api):
-    """A key far above its stream's first-tile max (in the second stream's tiles) sends the row
-    through the exact fallback over the whole split (the two streams are merged before the write)."""
+@pytest.mark.parametrize("factor,lo,hi", [
+    (2.5, 80, 64 + 96 - 12),    # ~100 nats above the rest: within the reference's 64-binade headroom
+    (3.0, 64 + 96 + 4, 64 + 128 - 12),  # the row sum passes 2^96: exact redo
+    (3.6, 64 + 128 + 4, 1e9),   # 2^(x - m_ref) overflows fp32: exact redo
+])
+def test_decode_overflow_fallback_rows(api, factor, lo, hi):
+    """A key far above its row's other scores, in the second stream's tiles: within the headroom it
+    is just a dominant key; past it the row goes through the exact redo over the whole split (the two
+    streams are merged before the write)."""
     x = I.make_custom(np.random.default_rng(59), [3000], [1], 64, 6000)
     # key 2920 sits in tile 91: local tile 91 of the one split (nsplit 1) and 29 of the third split
     # (nsplit 3 -> splits start at tiles 0, 31, 62), odd in both, so the second stream takes it.
-    # It is head 7's query with the span of the other 63 heads' queries projected out, times 2.5:
-    # ~92 nats for head 7 (2^(x - m_ref) overflows fp32), ~0 for every other head, and its v
-    # (dims 0..511) stays ~2.5 N(0,1), so head 7's exact redo is the only row it moves.
+    # It is head 7's query with the span of the other 63 heads' queries projected out, times
+    # `factor`: far above the rest for head 7, ~0 for every other head, and its v (dims 0..511)
+    # stays ~factor * N(0,1), so head 7 is the only row it moves.
     qh = oracle.bf16_bits_to_f64(x.q[0])
     others = np.delete(qh, 7, axis=0)
     coef, *_ = np.linalg.lstsq(others.T, qh[7], rcond=None)
     perp = qh[7] - others.T @ coef
-    x.kv_rows[2920] = I.f32_to_bf16_bits((2.5 * perp).astype(np.float32))
-    _run_check(api, x, 3, "decode overflow-inf")
-    _run_check(api, x, 1, "decode overflow-inf")
+    x.kv_rows[2920] = I.f32_to_bf16_bits((factor * perp).astype(np.float32))
+    qv = qh[7]
+    sc = x.scale * (oracle.bf16_bits_to_f64(x.kv_rows[:3000]) @ qv) / math.log(2.0)
+    margin = float(sc[2920] - np.max(np.delete(sc, 2920)))
+    assert lo < margin < hi, margin
+    _run_check(api, x, 3, f"decode planted x{factor}")
+    _run_check(api, x, 1, f"decode planted x{factor}")
 
 
 @pytest.mark.parametrize("workload", ["decode64k", "decode_batch16"])

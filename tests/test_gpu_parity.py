@@ -213,25 +213,65 @@ def test_request_alone_equals_request_in_batch(api):
         assert eo <= OUT_TOL and el <= LSE_TOL
 
 
+def planted_margin_log2(x, t, h, key):
+    """How far (in log2 units) the score of `key` for row (t, h) of request 0 lies above that row's
+    highest score over every other visible key.  Kernel 1's reference for a row is the highest score
+    of one tile of the split (at most that highest score) plus 64 binades, so a margin past 64 + 96
+    sends the row's sum past 2^96 (the exact redo) and one past 64 + 128 overflows the key's
+    2^(x - m_ref); below about 64 + 96 - 12 (N(0,1) scores: a tile's max lies within a few log2 units
+    of the row's) the row stays within the headroom."""
+    L, Q = int(x.seq_lens[0]), int(x.q_lens[0])
+    n = L - Q + t + 1
+    qv = oracle.bf16_bits_to_f64(x.q[t, h])
+    k = oracle.bf16_bits_to_f64(x.kv_rows[:n])
+    sc = x.scale * (k @ qv) / math.log(2.0)
+    return float(sc[key] - np.max(np.delete(sc, key)))
+
+
+def plant_key_for_row(x, t, h, key, factor):
+    """Key `key` of request 0 becomes `factor` times row (t, h)'s query with the span of the request's
+    other rows' queries projected out: it scores ~factor * 26 nats for that row and ~0 for every other
+    row, so no other row's output is pulled toward its (large) V row, whose bf16 rounding alone would
+    exceed the 1e-2 bar."""
+    Q = int(x.q_lens[0])
+    qh = oracle.bf16_bits_to_f64(x.q[:Q].reshape(Q * x.heads, -1))
+    r = t * x.heads + h
+    others = np.delete(qh, r, axis=0)
+    coef, *_ = np.linalg.lstsq(others.T, qh[r], rcond=None)
+    perp = qh[r] - others.T @ coef
+    x.kv_rows[key] = I.f32_to_bf16_bits((factor * perp).astype(np.float32))
+
+
+@pytest.mark.parametrize("form", FORMS)
+def test_dominant_key_within_headroom(api, form):
+    """A key ~100 log2 units above the rest of its row stays within the 64-binade headroom of the
+    fixed reference: no redo, and the row still matches the oracle."""
+    x = I.make_custom(np.random.default_rng(35), [2000], [4], 8, 4000)
+    plant_key_for_row(x, 0, 3, 1500, 1.8)
+    assert 80 < planted_margin_log2(x, 0, 3, 1500) < 64 + 96 - 12
+    _check(api, x, 2, "headroom", form)
+    _check(api, x, 1, "headroom", form)
+
+
 @pytest.mark.parametrize("form", FORMS)
 def test_overflow_fallback_rows(api, form):
-    """A key far above a row's first-block max sends the row through the exact fallback kernel."""
+    """A key ~173 log2 units (~120 nats) above the rest of its row: its p passes 2^96 relative to the
+    reference, so the row goes through the exact redo."""
     x = I.make_custom(np.random.default_rng(35), [2000], [4], 8, 4000)
-    q0 = oracle.bf16_bits_to_f64(x.q[0, 3])
-    # key 1500 aligned with (token 0, head 3): score ~ 1.6*|q|^2/sqrt(192) ~ 70 nats ~ 100 log2 units
-    x.kv_rows[1500] = I.f32_to_bf16_bits((1.6 * q0).astype(np.float32))
+    plant_key_for_row(x, 0, 3, 1500, 3.15)
+    m = planted_margin_log2(x, 0, 3, 1500)
+    assert 64 + 96 + 4 < m < 64 + 128 - 12, m
     _check(api, x, 2, "overflow", form)
     _check(api, x, 1, "overflow", form)
 
 
 @pytest.mark.parametrize("form", FORMS)
 def test_overflow_to_inf_fallback_rows(api, form):
-    """A key so far above the first tile's max that 2^(x - m_ref) overflows fp32:
-    without the exact fallback the row would come out inf/NaN."""
+    """A key so far above the rest of its row that 2^(x - m_ref) overflows fp32: without the exact
+    redo the row would come out inf/NaN."""
     x = I.make_custom(np.random.default_rng(39), [3000], [4], 8, 6000)
-    q0 = oracle.bf16_bits_to_f64(x.q[2, 5])
-    # key 2900 aligned with (token 2, head 5): score ~ 2.6*|q|^2/sqrt(192) ~ 108 nats ~ 156 log2 units
-    x.kv_rows[2900] = I.f32_to_bf16_bits((2.6 * q0).astype(np.float32))
+    plant_key_for_row(x, 2, 5, 2900, 4.3)
+    assert planted_margin_log2(x, 2, 5, 2900) > 64 + 128 + 4
     _check(api, x, 3, "overflow-inf", form)
     _check(api, x, 1, "overflow-inf", form)
 
