@@ -97,7 +97,7 @@ typedef struct {
 
 /*
  * Validate `cfg`, allocate the split workspace on the current device
- * (B * max_nsplit * ceil(Q_max*H/128)*128 rows of 512 bf16 partial outputs,
+ * (B * max_nsplit * ceil(Q_max*H/128)*128 rows of 512 fp16 partial outputs,
  * each normalised within its split, plus one fp32 log-sum-exp each) and
  * return a handle in *out.  Call outside graph capture.
  * Errors: INVALID_ARGUMENT (null, non-positive sizes, unknown form or flag), UNSUPPORTED (dims),
@@ -107,7 +107,9 @@ int mla_verify_create(const mla_verify_config* cfg, mla_verify_handle* out);
 
 /*
  * One verify-attention call: split partials (kernel 1) then their merge
- * (kernel 2), both on `stream`.
+ * (kernel 2), both on `stream`.  The split partials are fp16 (each row a
+ * convex combination of v rows, so every v entry must stay below 65504 in
+ * magnitude, which latent caches do by far), their LSEs fp32.
  *   q        device bf16 [T_q, H, 576], T_q = sum(q_lens), requests in order,
  *            rows 16-byte aligned (base pointer 16-byte aligned).
  *   kv_pool  device bf16 [num_slots, 576], row stride 1152 bytes, 16-byte aligned.
@@ -142,7 +144,7 @@ int mla_verify_run(mla_verify_handle h, const void* q, const void* kv_pool, cons
  * library runs on holds from the first use until the process ends.
  *   cfg      the shapes, as for mla_verify_create (read on every call; not kept).
  *   other arguments as in mla_verify_run; nsplit <= cfg->max_nsplit.
- * Size limit: B * nsplit * rows_pad * 512 bf16 partials (rows_pad = ceil(Q_max*H/128)*128, or 64
+ * Size limit: B * nsplit * rows_pad * 512 fp16 partials (rows_pad = ceil(Q_max*H/128)*128, or 64
  * when Q_max*H <= 64), then B * nsplit * rows_pad fp32 LSEs from the next 256-B boundary, must fit
  * the array; otherwise MLA_ERR_SCRATCH_TOO_SMALL and nothing is enqueued.  (One request of 1,024
  * rows at nsplit 32 takes 32.1 MiB; a 64-row decode step at nsplit 256 takes 16.1 MiB.)
@@ -252,7 +254,7 @@ int mla_verify_build_metadata(const int32_t* req_to_token, int32_t table_rows, i
 /*
  * Where a handle's split workspace lives (the partials kernel 1 writes and the
  * merge reads in mla_verify_run), for inspection and tests:
- *   *o_part   device bf16 [batch, max_nsplit, rows_pad, 512], rows_pad =
+ *   *o_part   device fp16 [batch, max_nsplit, rows_pad, 512], rows_pad =
  *             ceil(max_q_len * H / 128) * 128 (row r of request b is (token r / H,
  *             head r % H)); *o_part_bytes its size.
  *   *lse_part device fp32 [batch, max_nsplit, rows_pad]; *lse_part_bytes its size.

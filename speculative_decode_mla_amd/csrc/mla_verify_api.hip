@@ -19,7 +19,7 @@ struct mla_verify_s {
   int32_t cus;        // compute units of the device
   int32_t plan_ranges;  // 1: batches of 2..64 requests in the 128-row form use the range plan
   int32_t workers;      // range plan: workers, one workgroup per row group each (CUs / row groups)
-  uint16_t* o_part;  // bf16 [B, max_nsplit, rows_pad, 512]
+  uint16_t* o_part;  // fp16 [B, max_nsplit, rows_pad, 512]
   float* lse_part;  // [B, max_nsplit, rows_pad]
   int32_t* debug_flags;  // MLA_VERIFY_DEBUG builds: the device word of mla_verify_debug_flags (else null)
 };
@@ -307,7 +307,7 @@ int mla_verify_run_noalloc(const mla_verify_config* cfg, const void* q, const vo
   if (!aligned(q, 16) || !aligned(kv_pool, 16) || !aligned(slot_idx, 4) || !aligned(seq_lens, 4) ||
       !aligned(q_lens, 4) || !aligned(out, 16) || !aligned(lse, 4))
     return MLA_ERR_INVALID_ARGUMENT;
-  // The call's partials, laid out as in a handle's workspace for this nsplit: bf16 rows, then fp32
+  // The call's partials, laid out as in a handle's workspace for this nsplit: fp16 rows, then fp32
   // LSEs from the next 256-B boundary.
   const int64_t partial_rows = (int64_t)cfg->batch * nsplit * config_rows_pad(cfg);
   const int64_t o_bytes = partial_rows * mlav::kDv * (int64_t)sizeof(uint16_t);

@@ -24,7 +24,7 @@ struct PartialArgs {
   const int32_t* slot_idx;   // [sum L]
   const int32_t* seq_lens;   // [B]
   const int32_t* q_lens;     // [B]
-  uint16_t* o_part;          // bf16 [B, nsplit, rows_pad, 512], each row normalised within its split
+  uint16_t* o_part;          // fp16 [B, nsplit, rows_pad, 512], each row normalised within its split
   float* lse_part;           // fp32 [B, nsplit, rows_pad], natural log
   int32_t batch, heads, max_q_len, nsplit;
   int32_t row_groups;        // ceil(max_q_len*H / 128)
@@ -40,7 +40,7 @@ struct PartialArgs {
 
 // Kernel 2: one wave per (request, row); merges the row's split partials.
 struct MergeArgs {
-  const void* o_part;        // [B, nsplit, rows_stride, 512]: bf16 (the library's workspace) or fp32
+  const void* o_part;        // [B, nsplit, rows_stride, 512]: fp16 (the library's workspace) or fp32
   const float* lse_part;     // fp32 [B, nsplit, rows_stride]
   const int32_t* seq_lens;   // [B]; read only when use_all_splits == 0
   const int32_t* q_lens;     // [B]
@@ -48,7 +48,7 @@ struct MergeArgs {
   float* lse;                // fp32 [T_q*H]
   int32_t batch, heads, max_q_len, nsplit, rows_stride, min_tiles;
   int32_t use_all_splits;    // 1: merge all nsplit partials; 0: only the splits kernel 1 filled
-  int32_t part_fp32;         // 1: o_part holds fp32 values; 0: bf16
+  int32_t part_fp32;         // 1: o_part holds fp32 values; 0: fp16
   int32_t plan_ranges;       // 1: kernel 1 ran the range plan with `workers` workers (partials per request from it)
   int32_t workers;
   int32_t* debug_flags;      // as in PartialArgs

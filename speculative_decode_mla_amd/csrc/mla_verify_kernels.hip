@@ -45,6 +45,8 @@ namespace mlav {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -65,7 +67,7 @@ constexpr int kPvFrags = 2 * kHalfColBlocks;       // V^T fragments per wave per
 constexpr int kPrefetch = 4;                       // K fragment reads kept ahead of their MFMA
 constexpr int kVPrefetch = 4;                      // V^T fragment reads kept ahead
 constexpr int kDmaPerTile = 9;                     // direct-to-LDS loads per wave per tile
-constexpr int kStageRowBytes = 528;                // epilogue: one bf16 row half (512 B) + 16 B of padding
+constexpr int kStageRowBytes = 528;                // epilogue: one fp16 row half (512 B) + 16 B of padding
 constexpr int kStageBytes = 64 * kStageRowBytes;   // epilogue: one wave's 64 rows
 constexpr float kLn2 = 0.69314718055994530942f;
 static_assert(kTileKeys == 32 && kWaves * 8 == kTileKeys, "one 8-key block per wave per tile");
@@ -533,10 +535,10 @@ __device__ __forceinline__ void redo_rows_exact(const PartialArgs& p, const Work
     }
     const float inv = l > 0.f ? 1.0f / l : 0.f;
     const int64_t prow = part * p.rows_pad + row;
-    bf16x8 ov;
+    f16x8 ov;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) ov[j] = (__bf16)(acc[j] * inv);
-    *((bf16x8*)(p.o_part + prow * kDv) + lane) = ov;
+    for (int j = 0; j < 8; ++j) ov[j] = (_Float16)(acc[j] * inv);
+    *((f16x8*)(p.o_part + prow * kDv) + lane) = ov;
     if (lane == 0) p.lse_part[prow] = l > 0.f ? (m + __builtin_amdgcn_logf(l)) * kLn2 : -INFINITY;
   }
 }
@@ -908,7 +910,7 @@ __device__ __forceinline__ void partial_item(const PartialArgs& p, const WorkIte
   // between registers ahead of it.
   asm volatile(MLAV_MFMA_DRAIN);
 
-  // ---- partial write: o_s = O / l (bf16), lse_s = ln2 * (m_ref + log2 l) -----------------------
+  // ---- partial write: o_s = O / l (fp16), lse_s = ln2 * (m_ref + log2 l) -----------------------
   // The row sums live with the row's owner wave; swap them through LDS, together with
   // whether any row of the workgroup needs the exact redo.
   const float lt = pair_sum(st.l_run);
@@ -929,7 +931,7 @@ __device__ __forceinline__ void partial_item(const PartialArgs& p, const WorkIte
     // (le > 0 only if the reference is finite, and then m_ref = -nmref: one register less to keep)
     p.lse_part[(int64_t)wi.bs * p.rows_pad + myrow] = le > 0.f ? (__builtin_amdgcn_logf(le) - nmref) * kLn2 : -INFINITY;
 
-  // The wave's 64 rows x 256 columns go through the free ring as bf16 rows (stride
+  // The wave's 64 rows x 256 columns go through the free ring as fp16 rows (stride
   // kStageRowBytes, padded against bank conflicts), then out as whole 512-B row halves, two rows
   // per store instruction.  In the C layout the lane holds, per 32-column block c, columns
   // 32c + 8*q4 + 4*hi .. +3.  The wave's own rows (stage rows 0..31) are staged first and
@@ -937,13 +939,12 @@ __device__ __forceinline__ void partial_item(const PartialArgs& p, const WorkIte
   // under the conversion work.  Each half goes out as 16 LDS reads, one wait, then 16 stores:
   // a read, wait and store per row pair costs an LDS round trip per store (about 2 us a
   // workgroup).
-  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
   lds_char* stage = smem + w * kStageBytes;
   auto stage_block = [&](const f32x16& o, float inv, int row, int c, int q4) {
     const int cb = (32 * c + 8 * q4 + 4 * hi) * 2;
-    const bf16x4 v = {(__bf16)(acc_read(o[4 * q4]) * inv), (__bf16)(acc_read(o[4 * q4 + 1]) * inv),
-                      (__bf16)(acc_read(o[4 * q4 + 2]) * inv), (__bf16)(acc_read(o[4 * q4 + 3]) * inv)};
-    *(__attribute__((address_space(3))) bf16x4*)(stage + row * kStageRowBytes + cb) = v;
+    const f16x4 v = {(_Float16)(acc_read(o[4 * q4]) * inv), (_Float16)(acc_read(o[4 * q4 + 1]) * inv),
+                     (_Float16)(acc_read(o[4 * q4 + 2]) * inv), (_Float16)(acc_read(o[4 * q4 + 3]) * inv)};
+    *(__attribute__((address_space(3))) f16x4*)(stage + row * kStageRowBytes + cb) = v;
   };
   // (the column half from the wave index in a scalar register: keeping `half` live this long spilled it)
   uint16_t* part_base = p.o_part + (int64_t)wi.bs * p.rows_pad * kDv + (w_uniform & 1) * (kDv / 2) + (lane & 31) * 8;
@@ -1002,7 +1003,7 @@ void mla_verify_partial(PartialArgs p) {
 // partial sums are added through LDS.  Every thread keeps up to 8 loads in
 // flight, so the partials stream at memory speed.  Each wave also forms the
 // merge weights itself: M = max_s lse_s, w_s = exp(lse_s - M) / sum_s exp(lse_s - M).
-// PartT is __bf16 for the library's own workspace, float for caller partials.
+// PartT is _Float16 for the library's own workspace, float for caller partials.
 constexpr int kMergeUnroll = 8;
 // Split groups per workgroup (64 threads each): 4 in general.  A call with few rows and many
 // splits (a decode step has 64 rows) takes the column-sliced form below, which spreads a row over
@@ -1278,10 +1279,9 @@ void mla_verify_partial_2s(PartialArgs p) {
     p.lse_part[(int64_t)wi.bs * p.rows_pad + myrow] =
         co.lex > 0.f ? (co.m + __builtin_amdgcn_logf(co.lex)) * kLn2 : -INFINITY;
 
-  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
   // Both streams combine: in phase ph (column blocks 4ph .. 4ph+3 of the wave pair's 256 columns)
   // stream 0 combines blocks 4ph, 4ph+1 and stream 1 blocks 4ph+2, 4ph+3, each after taking the
-  // other stream's accumulators for its blocks through LDS; the bf16 rows meet in one staging area
+  // other stream's accumulators for its blocks through LDS; the fp16 rows meet in one staging area
   // per wave pair, and each stream stores 32 of its 64 rows.
   lds_char* stage = smem + (w & 1) * kStageBytes;
   constexpr int kDumpBytes = 16 * 1024;  // two column blocks, own and partner rows: 64 floats a lane
@@ -1319,14 +1319,14 @@ void mla_verify_partial_2s(PartialArgs p) {
         const f32x16& op = o_par[keep + cc];
         const int j = (cc * 4 + q4) * 2;
         const int cb = (32 * (keep + cc) + 8 * q4 + 4 * hi) * 2;
-        bf16x4 vo, vp;
+        f16x4 vo, vp;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          vo[e] = (__bf16)(acc_read(oo[4 * q4 + e]) * own_mine + dd[j][e] * own_other);
-          vp[e] = (__bf16)(acc_read(op[4 * q4 + e]) * par_mine + dd[j + 1][e] * par_other);
+          vo[e] = (_Float16)(acc_read(oo[4 * q4 + e]) * own_mine + dd[j][e] * own_other);
+          vp[e] = (_Float16)(acc_read(op[4 * q4 + e]) * par_mine + dd[j + 1][e] * par_other);
         }
-        *(__attribute__((address_space(3))) bf16x4*)(stage + lrow * kStageRowBytes + cb) = vo;
-        *(__attribute__((address_space(3))) bf16x4*)(stage + (32 + lrow) * kStageRowBytes + cb) = vp;
+        *(__attribute__((address_space(3))) f16x4*)(stage + lrow * kStageRowBytes + cb) = vo;
+        *(__attribute__((address_space(3))) f16x4*)(stage + (32 + lrow) * kStageRowBytes + cb) = vp;
       }
     if (ph == 0) __syncthreads();  // the hand-over area is read before phase 1 writes it again
   };
@@ -1370,12 +1370,10 @@ struct Raw8<float> {
   __device__ float get(int j) const { return j < 4 ? a[j] : b[j - 4]; }
 };
 template <>
-struct Raw8<__bf16> {
-  i32x4 a;
-  __device__ void load(const __bf16* src) { a = *(const i32x4*)src; }
-  __device__ float get(int j) const {
-    return (j & 1) ? __int_as_float(a[j >> 1] & (int)0xffff0000u) : __int_as_float(a[j >> 1] << 16);
-  }
+struct Raw8<_Float16> {
+  f16x8 a;
+  __device__ void load(const _Float16* src) { a = *(const f16x8*)src; }
+  __device__ float get(int j) const { return (float)a[j]; }
 };
 
 // kRowsPerBlock > 1 (with one split group): one wave per row, kRowsPerBlock consecutive rows of a
@@ -1611,13 +1609,13 @@ hipError_t launch_partial(const PartialArgs& a, hipStream_t stream) {
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream) {
   const int64_t rows = (int64_t)a.batch * a.max_q_len * a.heads;  // one workgroup per row below
   const bool few = rows < kMergeFewRows && a.nsplit >= kMergeManySplits;
-  // The library's bf16 partials with at most kMergeWaveSplits per row (the range plan, or a call such
+  // The library's fp16 partials with at most kMergeWaveSplits per row (the range plan, or a call such
   // as ctx64k's 32 splits): one wave per row, four rows per workgroup.  At ctx64k this took 0.7 us
   // less per call than 256 threads per row, measured on one box.
   if (a.plan_ranges || (!a.part_fp32 && !few && a.nsplit <= kMergeWaveSplits)) {
     constexpr int kRowsPerBlock = 4;
     const int64_t blocks = (int64_t)a.batch * ((a.max_q_len * a.heads + kRowsPerBlock - 1) / kRowsPerBlock);
-    hipLaunchKernelGGL((mla_verify_merge_kernel<__bf16, 1, kRowsPerBlock>), dim3((unsigned)blocks),
+    hipLaunchKernelGGL((mla_verify_merge_kernel<_Float16, 1, kRowsPerBlock>), dim3((unsigned)blocks),
                        dim3(64 * kRowsPerBlock), 0, stream, a);
     return hipGetLastError();
   }
@@ -1626,15 +1624,15 @@ hipError_t launch_merge(const MergeArgs& a, hipStream_t stream) {
     if (a.part_fp32)
       hipLaunchKernelGGL(mla_verify_merge_sliced<float>, grid, dim3(256), 0, stream, a);
     else
-      hipLaunchKernelGGL(mla_verify_merge_sliced<__bf16>, grid, dim3(256), 0, stream, a);
+      hipLaunchKernelGGL(mla_verify_merge_sliced<_Float16>, grid, dim3(256), 0, stream, a);
   } else if (a.part_fp32 && few)
     hipLaunchKernelGGL((mla_verify_merge_kernel<float, kMergeGroupsFew>), dim3((unsigned)rows), dim3(64 * kMergeGroupsFew), 0, stream, a);
   else if (a.part_fp32)
     hipLaunchKernelGGL((mla_verify_merge_kernel<float, 4>), dim3((unsigned)rows), dim3(256), 0, stream, a);
   else if (few)
-    hipLaunchKernelGGL((mla_verify_merge_kernel<__bf16, kMergeGroupsFew>), dim3((unsigned)rows), dim3(64 * kMergeGroupsFew), 0, stream, a);
+    hipLaunchKernelGGL((mla_verify_merge_kernel<_Float16, kMergeGroupsFew>), dim3((unsigned)rows), dim3(64 * kMergeGroupsFew), 0, stream, a);
   else
-    hipLaunchKernelGGL((mla_verify_merge_kernel<__bf16, 4>), dim3((unsigned)rows), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((mla_verify_merge_kernel<_Float16, 4>), dim3((unsigned)rows), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
