@@ -50,6 +50,7 @@ typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) char lds_char;
@@ -1279,63 +1280,85 @@ void mla_verify_partial_2s(PartialArgs p) {
     p.lse_part[(int64_t)wi.bs * p.rows_pad + myrow] =
         co.lex > 0.f ? (co.m + __builtin_amdgcn_logf(co.lex)) * kLn2 : -INFINITY;
 
-  // Both streams combine: in phase ph (column blocks 4ph .. 4ph+3 of the wave pair's 256 columns)
-  // stream 0 combines blocks 4ph, 4ph+1 and stream 1 blocks 4ph+2, 4ph+3, each after taking the
-  // other stream's accumulators for its blocks through LDS; the fp16 rows meet in one staging area
-  // per wave pair, and each stream stores 32 of its 64 rows.
+  // Both streams combine: of each group of four column blocks of the wave pair's 256 columns
+  // (4ph .. 4ph+3, ph = 0, 1), stream 0 combines blocks 4ph, 4ph+1 and stream 1 blocks 4ph+2,
+  // 4ph+3.  Each stream first hands the other its contribution to the other's blocks, already
+  // weighted (a_s / l) and rounded to fp16 (2^-12 of that contribution, far below the bf16 output's
+  // own rounding), through LDS; one barrier; then each adds what it received to its own weighted
+  // accumulators.  The fp16 rows meet in one staging area per wave pair, and each stream stores 32
+  // of its 64 rows.  (An fp32 hand-over of the raw accumulators, in two halves with a barrier
+  // each, moved twice the bytes through LDS.)
   lds_char* stage = smem + (w & 1) * kStageBytes;
-  constexpr int kDumpBytes = 16 * 1024;  // two column blocks, own and partner rows: 64 floats a lane
+  constexpr int kDumpBytes = 2 * 8 * 64 * 16;  // per wave: 2 groups x 8 (block, quad) x 64 lanes x 16 B
   static_assert(2 * kStageBytes + kWaves * kDumpBytes <= kRing * kTileBytes, "staging and hand-over fit the ring");
   lds_char* dump_mine = smem + 2 * kStageBytes + w * kDumpBytes;
   const lds_char* dump_other = smem + 2 * kStageBytes + (w ^ 2) * kDumpBytes;
-  // O = (O_0 a_0 + O_1 a_1) / l, with the division folded into the weights
-  const float own_mine = (stream == 0 ? co.a0 : co.a1) * co.inv, own_other = (stream == 0 ? co.a1 : co.a0) * co.inv;
-  const float par_mine = (stream == 0 ? cp.a0 : cp.a1) * cp.inv, par_other = (stream == 0 ? cp.a1 : cp.a0) * cp.inv;
-  auto epilogue_phase = [&](auto ph_c, auto stream_c) __attribute__((always_inline)) {
+  // O = (O_0 a_0 + O_1 a_1) / l, with the division folded into the weights; a stream weighs its
+  // own accumulators with *_mine for its own blocks and for the blocks it hands over alike
+  const float own_mine = (stream == 0 ? co.a0 : co.a1) * co.inv;
+  const float par_mine = (stream == 0 ? cp.a0 : cp.a1) * cp.inv;
+  auto give = [&](auto ph_c, auto stream_c) __attribute__((always_inline)) {
     constexpr int ph = decltype(ph_c)::value, S = decltype(stream_c)::value;
-    constexpr int give = 4 * ph + (S == 0 ? 2 : 0), keep = 4 * ph + (S == 0 ? 0 : 2);
+    constexpr int gb = 4 * ph + (S == 0 ? 2 : 0);
 #pragma unroll
     for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const f32x16& oo = o_own[give + cc];
-        const f32x16& op = o_par[give + cc];
-        const f32x4 vo = {acc_read(oo[4 * q4]), acc_read(oo[4 * q4 + 1]), acc_read(oo[4 * q4 + 2]), acc_read(oo[4 * q4 + 3])};
-        const f32x4 vp = {acc_read(op[4 * q4]), acc_read(op[4 * q4 + 1]), acc_read(op[4 * q4 + 2]), acc_read(op[4 * q4 + 3])};
-        const int j = (cc * 4 + q4) * 2;
-        *(__attribute__((address_space(3))) f32x4*)(dump_mine + (j * 64 + lane) * 16) = vo;
-        *(__attribute__((address_space(3))) f32x4*)(dump_mine + ((j + 1) * 64 + lane) * 16) = vp;
-      }
-    __syncthreads();  // both streams' hand-over halves are in LDS
-    f32x4 dd[16];     // all reads go out before any is used
-#pragma unroll
-    for (int j = 0; j < 16; ++j) dd[j] = *(const __attribute__((address_space(3))) f32x4*)(dump_other + (j * 64 + lane) * 16);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const f32x16& oo = o_own[keep + cc];
-        const f32x16& op = o_par[keep + cc];
-        const int j = (cc * 4 + q4) * 2;
-        const int cb = (32 * (keep + cc) + 8 * q4 + 4 * hi) * 2;
+        const f32x16& oo = o_own[gb + cc];
+        const f32x16& op = o_par[gb + cc];
         f16x4 vo, vp;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          vo[e] = (_Float16)(acc_read(oo[4 * q4 + e]) * own_mine + dd[j][e] * own_other);
-          vp[e] = (_Float16)(acc_read(op[4 * q4 + e]) * par_mine + dd[j + 1][e] * par_other);
+          vo[e] = (_Float16)(acc_read(oo[4 * q4 + e]) * own_mine);
+          vp[e] = (_Float16)(acc_read(op[4 * q4 + e]) * par_mine);
+        }
+        const i32x4 both = __builtin_shufflevector(__builtin_bit_cast(i32x2, vo), __builtin_bit_cast(i32x2, vp), 0, 1, 2, 3);
+        *(__attribute__((address_space(3))) i32x4*)(dump_mine + ((ph * 8 + cc * 4 + q4) * 64 + lane) * 16) = both;
+      }
+  };
+  auto keep = [&](auto ph_c, auto stream_c, const i32x4 (&dd)[16]) __attribute__((always_inline)) {
+    constexpr int ph = decltype(ph_c)::value, S = decltype(stream_c)::value;
+    constexpr int kb = 4 * ph + (S == 0 ? 0 : 2);
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x16& oo = o_own[kb + cc];
+        const f32x16& op = o_par[kb + cc];
+        const i32x4 d = dd[ph * 8 + cc * 4 + q4];
+        const f16x4 ro = __builtin_bit_cast(f16x4, (i32x2){d[0], d[1]});
+        const f16x4 rp = __builtin_bit_cast(f16x4, (i32x2){d[2], d[3]});
+        const int cb = (32 * (kb + cc) + 8 * q4 + 4 * hi) * 2;
+        f16x4 vo, vp;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          vo[e] = (_Float16)(acc_read(oo[4 * q4 + e]) * own_mine + (float)ro[e]);
+          vp[e] = (_Float16)(acc_read(op[4 * q4 + e]) * par_mine + (float)rp[e]);
         }
         *(__attribute__((address_space(3))) f16x4*)(stage + lrow * kStageRowBytes + cb) = vo;
         *(__attribute__((address_space(3))) f16x4*)(stage + (32 + lrow) * kStageRowBytes + cb) = vp;
       }
-    if (ph == 0) __syncthreads();  // the hand-over area is read before phase 1 writes it again
   };
   if (stream == 0) {
-    epilogue_phase(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
-    epilogue_phase(std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{});
+    give(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
+    give(std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{});
   } else {
-    epilogue_phase(std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{});
-    epilogue_phase(std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{});
+    give(std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{});
+    give(std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{});
+  }
+  __syncthreads();  // both streams' hand-overs are in LDS
+  {
+    i32x4 dd[16];  // all reads go out before any is used
+#pragma unroll
+    for (int j = 0; j < 16; ++j) dd[j] = *(const __attribute__((address_space(3))) i32x4*)(dump_other + (j * 64 + lane) * 16);
+    __builtin_amdgcn_sched_barrier(0);
+    if (stream == 0) {
+      keep(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, dd);
+      keep(std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{}, dd);
+    } else {
+      keep(std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{}, dd);
+      keep(std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{}, dd);
+    }
   }
   __syncthreads();  // both streams' columns are staged
   {
