@@ -1084,25 +1084,28 @@ void mla_verify_partial_2s(PartialArgs p) {
   // ---- prologue: slot indices of tile 0, the q rows, then tile 0 while the q rows land ----------
   // The two streams hold the same 64 rows, so the rows are staged once, through ring buffers 2 and 3
   // (rows of wave half h in buffer 2 + h, in the key-tile layout as in the 128-row form), and tile 0
-  // of each stream (buffers 0 and 1) is gathered while they arrive.  Both waves of a half issue the
-  // same q loads (the same bytes to the same place), which keeps the code free of branches between
-  // the untracked slot loads and their wait.  Tile 1 goes to buffers 2 and 3 in the first step,
-  // after the barrier that follows every wave's q reads.
+  // of each stream (buffers 0 and 1) is gathered while they arrive.  The two waves of a half split
+  // its 32 rows (wave (s, h) moves key blocks 2s, 2s + 1 of buffer 2 + h), so every wave issues the
+  // same number of loads and the waits below have fixed counts; each wave reads all 32 rows of its
+  // half after the barrier.  (With both waves moving all 32 rows, a workgroup moved 144 KiB for
+  // its 72 KiB of q, and the q rows were the last to land.)  Tile 1 goes to buffers 2 and 3 in the
+  // first step, after the barrier that follows every wave's q reads.
   int sl[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) sl[j] = load_b32_untracked(slots_g + gather_key(0, j));
-  static_assert(4 * kDmaPerTile == 36 && 2 * kDmaPerTile == 18, "wait counts below");
+  static_assert(2 * kDmaPerTile == 18, "wait counts below");
   {
     const uint32_t qbuf = smem_base + (2 + (w_uniform & 1)) * kTileBytes;
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
+    for (int k = 0; k < 2; ++k) {
+      const int kb = 2 * (w_uniform >> 1) + k;
       const int r = row0 + half * kRowsPerWave + 8 * kb + g_kr;
       const int64_t qrow = wi.qo * H + (r < R ? r : 0);
       dma_key_block((const char*)(p.q + qrow * kDqk) + (((lane & 7) ^ g_kr ^ (kb & 1)) << 4), qbuf + kb * kKeyBlockBytes);
     }
   }
-  // the slot indices have landed (the 36 q loads issued after them may still be in flight)
-  asm volatile("s_waitcnt vmcnt(36)" : "+v"(sl[0]), "+v"(sl[1]) : : "memory");
+  // the slot indices have landed (the 18 q loads issued after them may still be in flight)
+  asm volatile("s_waitcnt vmcnt(18)" : "+v"(sl[0]), "+v"(sl[1]) : : "memory");
 #pragma unroll
   for (int j = 0; j < 2; ++j) sl[j] = checked_slot(sl[j], p.num_slots, p.debug_flags);
   if (nst > 0) {
