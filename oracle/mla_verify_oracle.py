@@ -39,8 +39,6 @@ All arithmetic is float64 on bf16-decoded inputs.
 """
 from __future__ import annotations
 
-import math
-
 import numpy as np
 
 D_QK = 576
