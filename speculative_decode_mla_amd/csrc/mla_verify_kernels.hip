@@ -240,6 +240,12 @@ __device__ __forceinline__ void dma16(const void* gsrc, uint32_t m0_value) {
 }
 #pragma clang diagnostic pop
 
+// 16-byte store with the agent-coherence bit (sc1): written through to memory rather than left
+// dirty in this XCD's L2, where the end of the kernel would have to write it back.
+__device__ __forceinline__ void store16_through(void* dst, const i32x4& v) {
+  asm volatile("global_store_dwordx4 %0, %1, off sc1" : : "v"(dst), "v"(v) : "memory");
+}
+
 // One wave's share of a tile: key block w (8 keys x 1152 B) as nine 1 KiB loads;
 // load cg moves 16-B chunks [8cg, 8cg+8) of the eight rows (see the layout above).
 // dma_chunk_group issues load cg alone (cg a compile-time constant after unrolling).
@@ -959,7 +965,7 @@ __device__ __forceinline__ void partial_item(const PartialArgs& p, const WorkIte
     for (int k = 0; k < 16; ++k) {
       const int grow = grow0 + 2 * k + hi;
       // (nontemporal: the merge reads the partials from another XCD, not from this L2)
-      if (grow < R) __builtin_nontemporal_store(v[k], (i32x4*)(part_base + (int64_t)grow * kDv));
+      if (grow < R) store16_through(part_base + (int64_t)grow * kDv, v[k]);
     }
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -1378,7 +1384,7 @@ void mla_verify_partial_2s(PartialArgs p) {
     for (int k = 0; k < 16; ++k) {
       const int r = rbase + 2 * k + hi;
       const int grow = row0 + (r < 32 ? half * kRowsPerWave + r : (1 - half) * kRowsPerWave + r - 32);
-      if (grow < R) *(i32x4*)(part_base + (int64_t)grow * kDv) = sv[k];
+      if (grow < R) store16_through(part_base + (int64_t)grow * kDv, sv[k]);
     }
   }
   if (any_redo) {
