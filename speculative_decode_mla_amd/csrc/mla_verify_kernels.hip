@@ -964,7 +964,7 @@ __device__ __forceinline__ void partial_item(const PartialArgs& p, const WorkIte
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
       const int grow = grow0 + 2 * k + hi;
-      // (nontemporal: the merge reads the partials from another XCD, not from this L2)
+      // (written through: the merge reads the partials from another XCD, not from this L2)
       if (grow < R) store16_through(part_base + (int64_t)grow * kDv, v[k]);
     }
     __builtin_amdgcn_sched_barrier(0);
