@@ -29,6 +29,8 @@ COMMON_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17",
     # keep packed fp32 VALU ops out of the generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # the leading kernel arguments (kernel 1's lengths and sizes) arrive in scalar registers
+    "-mllvm", "-amdgpu-kernarg-preload-count=7",
     "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"),
 ]
 

@@ -991,9 +991,26 @@ __device__ __forceinline__ void partial_item(const PartialArgs& p, const WorkIte
 // Kernel 1, 128-row form.  kRanges = false: one workgroup per (request, split, row group), splits
 // of equal length per request.  kRanges = true: the range plan above, one workgroup per (piece,
 // row group).
+// The arguments the workgroup's first loads depend on come first and separately (the lengths'
+// addresses and the sizes the work decode reads): the build preloads the leading kernel arguments
+// into scalar registers, so the lengths are requested without waiting for the argument block.
+#define MLAV_LEAD_ARGS const int32_t *seq_lens, const int32_t *q_lens, int32_t batch, int32_t nsplit, \
+                       int32_t row_groups, int32_t min_tiles, int32_t max_q_len
+#define MLAV_LEAD_INTO(p)   \
+  p.seq_lens = seq_lens;    \
+  p.q_lens = q_lens;        \
+  p.batch = batch;          \
+  p.nsplit = nsplit;        \
+  p.row_groups = row_groups; \
+  p.min_tiles = min_tiles;  \
+  p.max_q_len = max_q_len
+#define MLAV_LEAD_OF(a) a.seq_lens, a.q_lens, a.batch, a.nsplit, a.row_groups, a.min_tiles, a.max_q_len
+
 template <bool kRanges>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
-void mla_verify_partial(PartialArgs p) {
+void mla_verify_partial(MLAV_LEAD_ARGS, PartialArgs args) {
+  PartialArgs p = args;
+  MLAV_LEAD_INTO(p);
   if constexpr (!kRanges) {
     WorkItem wi;
     if (!decode_work(p, blockIdx.x, kRowsPerGroup, wi)) return;
@@ -1036,7 +1053,9 @@ constexpr int kMergeWaveSplits = 32;    // up to this many splits: one wave per 
 // tile.)  At the end the two streams are merged inside the workgroup and one partial per split is
 // written, as in the 128-row form.
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
-void mla_verify_partial_2s(PartialArgs p) {
+void mla_verify_partial_2s(MLAV_LEAD_ARGS, PartialArgs args) {
+  PartialArgs p = args;
+  MLAV_LEAD_INTO(p);
   __shared__ __attribute__((aligned(1024))) char smem_raw[kRing * kTileBytes + kXchgBytes];
   lds_char* smem = (lds_char*)smem_raw;
   lds_char* xchg = smem + kRing * kTileBytes;  // [2][kWaves][2 KiB]: bf16 P of each wave, double-buffered
@@ -1627,14 +1646,14 @@ __global__ __launch_bounds__(256) void mla_verify_merge_sliced(MergeArgs p) {
 hipError_t launch_partial(const PartialArgs& a, hipStream_t stream) {
   if (a.plan_ranges) {
     const int64_t grid = range_grid(a.workers, a.row_groups, a.batch);
-    hipLaunchKernelGGL(mla_verify_partial<true>, dim3((unsigned)grid), dim3(kWaves * 64), 0, stream, a);
+    hipLaunchKernelGGL(mla_verify_partial<true>, dim3((unsigned)grid), dim3(kWaves * 64), 0, stream, MLAV_LEAD_OF(a), a);
     return hipGetLastError();
   }
   const int64_t grid = (int64_t)a.batch * a.nsplit * a.row_groups;
   if (a.streams == 2)
-    hipLaunchKernelGGL(mla_verify_partial_2s, dim3((unsigned)grid), dim3(kWaves * 64), 0, stream, a);
+    hipLaunchKernelGGL(mla_verify_partial_2s, dim3((unsigned)grid), dim3(kWaves * 64), 0, stream, MLAV_LEAD_OF(a), a);
   else
-    hipLaunchKernelGGL(mla_verify_partial<false>, dim3((unsigned)grid), dim3(kWaves * 64), 0, stream, a);
+    hipLaunchKernelGGL(mla_verify_partial<false>, dim3((unsigned)grid), dim3(kWaves * 64), 0, stream, MLAV_LEAD_OF(a), a);
   return hipGetLastError();
 }
 
