@@ -253,6 +253,77 @@ def bench_metadata(args, w, x, h, q, pool, slot_idx, seq_lens, q_lens, out, lse,
     print(json.dumps(res), flush=True)
 
 
+def _smi_sample(delay_s: float):
+    """Start a read-only `amd-smi metric` sample of socket power and the XCD clocks, taken delay_s
+    from now; returns a function that collects it ({} when the tool is absent or fails)."""
+    import subprocess
+    try:
+        proc = subprocess.Popen(["bash", "-c", f"sleep {delay_s}; timeout -k 5 20 amd-smi metric -g 0 -p -c"],
+                                stdout=subprocess.PIPE, stderr=subprocess.DEVNULL, text=True)
+    except OSError:
+        return lambda: {}
+
+    def collect():
+        text = proc.communicate()[0]
+        power = [l.split(":", 1)[1].strip() for l in text.splitlines() if "SOCKET_POWER" in l]
+        clk, in_gfx = [], False  # the CLK line of each GFX_<n> block (one per XCD), not the other clocks
+        for l in text.splitlines():
+            t = l.strip()
+            if t.startswith("GFX_") and t.endswith(":"):
+                in_gfx = True
+            elif in_gfx and t.startswith("CLK:"):
+                clk.append(t.split()[1])
+                in_gfx = False
+        out = {}
+        if power and power[0].endswith("W") and power[0][:-1].strip().isdigit():
+            out["socket_power_w"] = int(power[0][:-1])
+        clk = [int(c) for c in clk if c.isdigit()]
+        if clk:
+            out["xcd_clock_mhz"] = clk
+        return out
+    return collect
+
+
+def bench_mfma_ceiling(torch):
+    """What dense bf16 MFMA work sustains on this GPU with random data: the vendor GEMM
+    (torch.matmul, i.e. hipBLASLt) on N(0,1) operands for a few large shapes, each after 1 s of
+    untimed GEMMs and timed over 2.5 s, with one power and clock sample in the middle.  MFMA power
+    depends on the operand bits, so with random data the chip runs at its power limit below its
+    top clock; this is the practical ceiling against which kernel 1's fraction of the published
+    2.5 PFLOP/s can be read."""
+    gen = torch.Generator(device="cuda").manual_seed(0)
+    rows = []
+    for m, n, k in [(8192, 8192, 8192), (16384, 16384, 8192), (4096, 4096, 16384)]:
+        a = torch.randn(m, k, device="cuda", dtype=torch.bfloat16, generator=gen)
+        b = torch.randn(k, n, device="cuda", dtype=torch.bfloat16, generator=gen)
+        c = torch.empty(m, n, device="cuda", dtype=torch.bfloat16)
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < 1.0:
+            for _ in range(10):
+                torch.matmul(a, b, out=c)
+            torch.cuda.synchronize()
+        sample = _smi_sample(1.0)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 0
+        e0.record()
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < 2.5:
+            for _ in range(20):
+                torch.matmul(a, b, out=c)
+            reps += 20
+            torch.cuda.synchronize()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        tflops = 2.0 * m * n * k / us / 1e6
+        rows.append({"shape_mnk": [m, n, k], "us": round(us, 1), "tflops": round(tflops, 1),
+                     "frac_of_2500": round(tflops / 2500.0, 4), **sample()})
+        print(f"# {m}x{n}x{k}: {us:.1f} us, {tflops:.0f} TFLOP/s", file=sys.stderr, flush=True)
+        del a, b, c
+    print(json.dumps({"mfma_ceiling": rows, "what": "torch.matmul bf16 (hipBLASLt), N(0,1) operands",
+                      "peak_tflops": 2500.0}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -271,6 +342,11 @@ def main():
     ap.add_argument("--eager", action="store_true", help="plain launches, no graph (for profilers)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run a plain 256 MiB device copy (reference size for HBM traffic counters)")
+    ap.add_argument("--power-window", type=float, default=2.0,
+                    help="seconds of back-to-back calls after the timed region with one amd-smi power and clock "
+                         "sample in the middle (0: none)")
+    ap.add_argument("--mfma-ceiling", action="store_true",
+                    help="only time the vendor bf16 GEMM on random data (the MFMA rate this GPU sustains)")
     ap.add_argument("--metadata", action="store_true",
                     help="measure the device-side step-metadata build for the workload instead")
     ap.add_argument("--compact", action="store_true",
@@ -298,6 +374,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": n, "launches": 3}))
+        return
+    if args.mfma_ceiling:
+        bench_mfma_ceiling(torch)
         return
     w = I.WORKLOADS[args.workload]
     nsplit = args.nsplit or w.nsplit
@@ -343,6 +422,7 @@ def main():
 
     stream = torch.cuda.current_stream()
     settle_s, settle_calls = 0.0, 0
+    power = {}
     if args.eager:
         for _ in range(args.warmup):
             step()
@@ -425,6 +505,19 @@ def main():
             b.record(stream)
         torch.cuda.synchronize()
         k1_us = statistics.median(a.elapsed_time(b) * 1e3 / 10 for a, b in kev)
+        # Socket power and XCD clocks while the call runs back to back (read-only amd-smi query, after
+        # the timed region so that it cannot disturb it): MFMA power grows with the operand bits, and
+        # with random data the GPU reaches its power limit below its top clock.
+        if args.power_window > 0:
+            sample = _smi_sample(args.power_window / 2)
+            t_pw = time.perf_counter()
+            while time.perf_counter() - t_pw < args.power_window:
+                for _ in range(10):
+                    gs.replay()
+                torch.cuda.synchronize()
+            power = sample()
+            if power:
+                power["during"] = f"{args.power_window:g} s of back-to-back calls after the timed region"
         # (last: the flushes disturb the timings that follow them)
         # cold single calls: 1 GiB read before each replay (outside the events) evicts the KV rows from
         # the L2s and the 256 MB MALL, so the call reads them from HBM.  A read, not a write: written
@@ -507,6 +600,7 @@ def main():
         "partial_kernel_us": round(k1_us, 3) if k1_us == k1_us else None,
         "parity_sampled": {"rows": len(rows), "max_abs_err_out": err_o, "max_abs_err_lse": err_l},
         "roofline": roofline,
+        "power_sample": power,
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(x, args.cpu_budget)
