@@ -955,7 +955,10 @@ __device__ __forceinline__ void partial_item(const PartialArgs& p, const WorkIte
   };
   // (the column half from the wave index in a scalar register: keeping `half` live this long spilled it)
   uint16_t* part_base = p.o_part + (int64_t)wi.bs * p.rows_pad * kDv + (w_uniform & 1) * (kDv / 2) + (lane & 31) * 8;
-  auto store_half = [&](const int r0, const int grow0) {  // stage rows r0 .. r0+31 = rows grow0 ..
+  // `between(k)` runs after the k-th store: the stores of the own rows go out between the
+  // conversions of the partner's rows (the CU's store path and the VALU then work at once;
+  // one after the other, the conversion and the store issue each took about 1 us).
+  auto store_half = [&](const int r0, const int grow0, auto between) {  // stage rows r0 .. r0+31 = rows grow0 ..
     i32x4 v[16];
 #pragma unroll
     for (int k = 0; k < 16; ++k)
@@ -966,19 +969,19 @@ __device__ __forceinline__ void partial_item(const PartialArgs& p, const WorkIte
       const int grow = grow0 + 2 * k + hi;
       // (written through: the merge reads the partials from another XCD, not from this L2)
       if (grow < R) store16_through(part_base + (int64_t)grow * kDv, v[k]);
+      between(k);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_sched_barrier(0);
   };
 #pragma unroll
   for (int c = 0; c < kHalfColBlocks; ++c)
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) stage_block(o_own[c], inv_own, lrow, c, q4);
-  store_half(0, row0 + w * kRowsPerWave);
+  store_half(0, row0 + w * kRowsPerWave, [&](int k) {  // two of the 32 partner blocks per store
 #pragma unroll
-  for (int c = 0; c < kHalfColBlocks; ++c)
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) stage_block(o_par[c], inv_par, 32 + lrow, c, q4);
-  store_half(32, row0 + partner * kRowsPerWave);
+    for (int b = 2 * k; b < 2 * k + 2; ++b) stage_block(o_par[b >> 2], inv_par, 32 + lrow, b >> 2, b & 3);
+  });
+  store_half(32, row0 + partner * kRowsPerWave, [](int) {});
 
   // Rows whose sums outgrew the fixed reference are redone exactly by their owner wave,
   // once both halves of the row have been written.
