@@ -1042,18 +1042,18 @@ constexpr int kMergeFewRows = 512;      // fewer rows per call than this ...
 constexpr int kMergeManySplits = 64;    // ... and at least this many splits: the forms for few rows
 constexpr int kMergeWaveSplits = 32;    // up to this many splits: one wave per row
 
-// Eight consecutive partial values: loaded raw (so that a batch of loads is in flight at
-// once), widened to fp32 when used.
 // Kernel 1, two-stream form, for requests of at most 64 (token, head) rows (a q_len = 1 decode
 // step with H <= 64, or a few draft tokens with few heads).  A 128-row workgroup would spend half
 // of its MFMA work on rows that do not exist; here the four waves form two streams of a wave pair,
-// both over the same 64 rows (wave 2s + h: stream s, rows [32h, 32h + 32), output columns
-// [256h, 256h + 256)).  Stream s takes tiles s, s + 2, s + 4, ... of the split, so one step consumes
-// two tiles.  Each stream's tiles are double-buffered in two of the four ring buffers: the next
-// tile is gathered between the Q.K MFMAs of the current one, into the buffer every wave finished
-// with at the step's first barrier.  (The one-tile-ahead Q.K of the 128-row form would need three
-// buffers per stream, which do not fit, so here the softmax sits between the two contractions of a
-// tile.)  At the end the two streams are merged inside the workgroup and one partial per split is
+// both over the same 64 rows (wave 2s + h: stream s, rows [32h, 32h + 32), all 512 output
+// columns).  Stream s takes tiles s, s + 2, s + 4, ... of the split, so one step consumes two
+// tiles.  Each stream's tiles are double-buffered in two of the four ring buffers: the next tile is
+// gathered between the Q.K MFMAs of the current one, into the buffer every wave finished with at
+// the step's barrier.  (The one-tile-ahead Q.K of the 128-row form would need three buffers per
+// stream, which do not fit, so here the softmax sits between the two contractions of a tile.)
+// Each wave's P.V covers its own rows only, so no wave waits for another's P: the half of the
+// softmax that the first 16-key step needs runs before the P.V MFMAs, the other half between them.
+// At the end the two streams are merged inside the workgroup and one partial per split is
 // written, as in the 128-row form.
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void mla_verify_partial_2s(MLAV_LEAD_ARGS, PartialArgs args) {
@@ -1061,7 +1061,6 @@ void mla_verify_partial_2s(MLAV_LEAD_ARGS, PartialArgs args) {
   MLAV_LEAD_INTO(p);
   __shared__ __attribute__((aligned(1024))) char smem_raw[kRing * kTileBytes + kXchgBytes];
   lds_char* smem = (lds_char*)smem_raw;
-  lds_char* xchg = smem + kRing * kTileBytes;  // [2][kWaves][2 KiB]: bf16 P of each wave, double-buffered
 
   WorkItem wi;
   if (!decode_work(p, blockIdx.x, kRowsPerGroup2s, wi)) return;
@@ -1072,7 +1071,6 @@ void mla_verify_partial_2s(MLAV_LEAD_ARGS, PartialArgs args) {
   const int hi = lane >> 5, lrow = lane & 31;
   const int stream = w >> 1;
   const int half = w & 1;
-  const int partner = w ^ 1;
   const int row0 = wi.g * kRowsPerGroup2s;
   const int myrow = row0 + half * kRowsPerWave + lrow;
   const bool row_valid = myrow < R;
@@ -1156,7 +1154,7 @@ void mla_verify_partial_2s(MLAV_LEAD_ARGS, PartialArgs args) {
 #pragma unroll
   for (int j = 0; j < 2; ++j) sn[j] = slots_g[gather_key(1, j)];
 
-  // P.V A operand addresses, as in the 128-row form (this wave's column half folded in)
+  // P.V A operand addresses, as in the 128-row form (the column block's offset is added per read)
   int vaddr[2][2];
   {
     const int G = lane >> 4, j = lane & 15;
@@ -1166,17 +1164,16 @@ void mla_verify_partial_2s(MLAV_LEAD_ARGS, PartialArgs args) {
     for (int e = 0; e < 2; ++e)
 #pragma unroll
       for (int r = 0; r < 2; ++r)
-        vaddr[e][r] = half * 4 * kBlockBytes + r * kKeyBlockBytes + kr * 128 + (((4 * e) ^ u ^ kr ^ r) << 4) +
-                      (j & 1) * 8;
+        vaddr[e][r] = r * kKeyBlockBytes + kr * 128 + (((4 * e) ^ u ^ kr ^ r) << 4) + (j & 1) * 8;
   }
-  f32x16 o_own[kHalfColBlocks], o_par[kHalfColBlocks];
+  // O^T of the wave's 32 rows, all 512 columns (column block c: columns 32c .. 32c + 31)
+  f32x16 o_acc[kColBlocks];
 #pragma unroll
-  for (int c = 0; c < kHalfColBlocks; ++c) {
-    o_own[c] = (f32x16){};
-    o_par[c] = (f32x16){};
+  for (int c = 0; c < kColBlocks; ++c) {
+    o_acc[c] = (f32x16){};
     // zeroed here, in AGPRs: left alone, the compiler moved the zeroing down to just before the
     // first P.V MFMA inside the loop, with no wait states between the write and the MFMA
-    asm volatile("" : "+a"(o_own[c]), "+a"(o_par[c]));
+    asm volatile("" : "+a"(o_acc[c]));
   }
   RowSoftmax st{-INFINITY, 0.f, 0.f};
   float nmref = 0.f;
@@ -1184,14 +1181,16 @@ void mla_verify_partial_2s(MLAV_LEAD_ARGS, PartialArgs args) {
   auto kread = [&](const lds_char* tb, int ks) {
     kf[ks] = *(const __attribute__((address_space(3))) bf16x8*)(tb + kaddr[ks & 3] + (ks >> 2) * kBlockBytes);
   };
-  bf16x8 vf[kPvFrags];
+  // V^T fragment n of a tile: column block n % 16, 16-key step n / 16
+  constexpr int kPvFrags2s = 2 * kColBlocks;
+  bf16x8 vf[kPvFrags2s];
   auto vread = [&](const lds_char* tb, int n) {
-    const int cbl = n & (kHalfColBlocks - 1), kk = n >> 3;
-    const lds_char* vb = tb + (cbl >> 1) * kBlockBytes + kk * 2 * kKeyBlockBytes;
+    const int cb = n & (kColBlocks - 1), kk = n >> 4;
+    const lds_char* vb = tb + (cb >> 1) * kBlockBytes + kk * 2 * kKeyBlockBytes;
     const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) i16x4*)(vb + vaddr[cbl & 1][0]));
+        (__attribute__((address_space(3))) i16x4*)(vb + vaddr[cb & 1][0]));
     const i16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) i16x4*)(vb + vaddr[cbl & 1][1]));
+        (__attribute__((address_space(3))) i16x4*)(vb + vaddr[cb & 1][1]));
     vf[n] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
   };
 
@@ -1208,9 +1207,8 @@ void mla_verify_partial_2s(MLAV_LEAD_ARGS, PartialArgs args) {
       for (int j = 0; j < 2; ++j) sn[j] = slots_g[gather_key(k + 2, j)];
     }
     const uint32_t l0 = g_lds(k + 1, 0), l1 = g_lds(k + 1, 1);
-    SoftmaxTile sm;
-    lds_char* xw = xchg + (k & 1) * (kWaves * 2048) + w * 2048 + lane * 16;
     if (active) {
+      SoftmaxTile sm;
       // Q.K of tile k, the gathers of the stream's tile k+1 between its MFMAs
       f32x16 sacc;
 #pragma unroll
@@ -1237,33 +1235,38 @@ void mla_verify_partial_2s(MLAV_LEAD_ARGS, PartialArgs args) {
         st.m_ref = tile_row_max(sacc) * p.scale_log2 + kRefHeadroom;
         nmref = (st.m_ref == -INFINITY) ? 0.f : -st.m_ref;
       }
-      scale_scores(sm, sacc, nmref, p.scale_log2);
-#pragma unroll
-      for (int slot = 0; slot < kSoftmaxSlots; ++slot) softmax_slot(slot, sm);
-      *(__attribute__((address_space(3))) i32x4*)(xw) = sm.operand(0);
-      *(__attribute__((address_space(3))) i32x4*)(xw + 1024) = sm.operand(1);
-    }
-    __syncthreads();  // the partner's P is visible
-    if (active) {
-      const bf16x8 pown[2] = {__builtin_bit_cast(bf16x8, sm.operand(0)), __builtin_bit_cast(bf16x8, sm.operand(1))};
-      bf16x8 ppar[2];
-      {
-        const lds_char* xp = xchg + (k & 1) * (kWaves * 2048) + partner * 2048 + lane * 16;
-        ppar[0] = *(const __attribute__((address_space(3))) bf16x8*)(xp);
-        ppar[1] = *(const __attribute__((address_space(3))) bf16x8*)(xp + 1024);
-      }
+      // The first V^T fragments go out now and land during the first half of the softmax: the
+      // lane's scores 0..7 (keys 0..15 of the tile, what the first 16 P.V MFMAs take)
 #pragma unroll
       for (int n = 0; n < kVPrefetch; ++n) vread(tb, n);
 #pragma unroll
-      for (int n = 0; n < kPvFrags; ++n) {
+      for (int j = 0; j < 8; ++j) sm.s[j] = vfma(sacc[j], p.scale_log2, nmref);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) sm.s[j] = vexp2(sm.s[j]);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) sm.pw[m] = vpack_bf16(sm.s[2 * m], sm.s[2 * m + 1]);
+      asm volatile("s_nop 3");  // wait states between the last bf16 pair and the first MFMA reading it
+      const bf16x8 p0 = __builtin_bit_cast(bf16x8, sm.operand(0));
+      bf16x8 p1;
+      // P.V of the wave's rows over all 32 column-block fragments: between the first 16 MFMAs the
+      // second half of the softmax (scores 8..15: FMA and exp2 in slots 0..7, the bf16 pairs in
+      // slots 8..11, four slots before the first MFMA that takes them), between the last 16 the
+      // row sums
+#pragma unroll
+      for (int n = 0; n < kPvFrags2s; ++n) {
         __builtin_amdgcn_sched_barrier(0);
-        if (n + kVPrefetch < kPvFrags) vread(tb, n + kVPrefetch);
+        if (n + kVPrefetch < kPvFrags2s) vread(tb, n + kVPrefetch);
         __builtin_amdgcn_sched_barrier(0);
-        mfma_acc_a(o_own[n & (kHalfColBlocks - 1)], vf[n], pown[n >> 3]);
+        mfma_acc_a(o_acc[n & (kColBlocks - 1)], vf[n], n < kColBlocks ? p0 : p1);
         __builtin_amdgcn_sched_barrier(0);
-        sum_slot(n, sm, st);
-        __builtin_amdgcn_sched_barrier(0);
-        mfma_acc_a(o_par[n & (kHalfColBlocks - 1)], vf[n], ppar[n >> 3]);
+        if (n < 8) {
+          sm.s[8 + n] = vexp2(vfma(sacc[8 + n], p.scale_log2, nmref));
+        } else if (n < 12) {
+          sm.pw[n - 4] = vpack_bf16(sm.s[2 * n - 8], sm.s[2 * n - 7]);
+          if (n == 11) p1 = __builtin_bit_cast(bf16x8, sm.operand(1));
+        } else if (n >= kColBlocks) {
+          sum_slot(n - kColBlocks, sm, st);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -1280,7 +1283,7 @@ void mla_verify_partial_2s(MLAV_LEAD_ARGS, PartialArgs args) {
   // either stream's sum outgrew its reference is redone exactly over the whole split.
   const float lt = pair_sum(st.l_run);
   const float le = pair_sum(st.l_exact);
-  __syncthreads();  // every wave is done with the ring and the P exchange buffers
+  __syncthreads();  // every wave is done with the ring
   float* stat = (float*)(smem_raw + kRing * kTileBytes);  // [wave][32 rows][3]: m_ref, l, l_exact
   if (hi == 0) {
     stat[(w * 32 + lrow) * 3 + 0] = st.m_ref;
@@ -1288,12 +1291,11 @@ void mla_verify_partial_2s(MLAV_LEAD_ARGS, PartialArgs args) {
     stat[(w * 32 + lrow) * 3 + 2] = le;
   }
   __syncthreads();
-  // this lane's own row (32*half + lrow) and partner row (32*(1-half) + lrow): stream 0 holds them
-  // in waves half and 1-half, stream 1 in waves 2+half and 3-half
+  // row 32*hh + lrow: stream 0 holds it in wave hh, stream 1 in wave 2 + hh
   struct Comb { float a0, a1, inv, lex, m; bool redo; };
-  auto combine = [&](int wa) {
-    const float* s0 = stat + (wa * 32 + lrow) * 3;
-    const float* s1 = stat + ((wa + 2) * 32 + lrow) * 3;
+  auto combine = [&](int hh) {
+    const float* s0 = stat + (hh * 32 + lrow) * 3;
+    const float* s1 = stat + ((hh + 2) * 32 + lrow) * 3;
     Comb c;
     c.m = fmaxf(s0[0], s1[0]);
     c.a0 = s0[0] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s0[0] - c.m);
@@ -1304,108 +1306,84 @@ void mla_verify_partial_2s(MLAV_LEAD_ARGS, PartialArgs args) {
     c.redo = !(s0[2] < kRowSumLimit) || !(s1[2] < kRowSumLimit);  // incl. +inf / NaN
     return c;
   };
-  const Comb co = combine(half), cp = combine(1 - half);
-  const bool any_redo = __ballot(co.redo || cp.redo) != 0;  // the wave's lanes cover all 64 rows
+  const Comb co = combine(half);
+  // (the other half's rows too, so that every wave sees the same answer for the barrier below)
+  const bool any_redo = __ballot(co.redo || combine(1 - half).redo) != 0;
   const uint64_t redo = __ballot(co.redo && hi == 0 && row_valid);
   if (stream == 0 && row_valid && hi == 0)
     p.lse_part[(int64_t)wi.bs * p.rows_pad + myrow] =
         co.lex > 0.f ? (co.m + __builtin_amdgcn_logf(co.lex)) * kLn2 : -INFINITY;
 
-  // Both streams combine: of each group of four column blocks of the wave pair's 256 columns
-  // (4ph .. 4ph+3, ph = 0, 1), stream 0 combines blocks 4ph, 4ph+1 and stream 1 blocks 4ph+2,
-  // 4ph+3.  Each stream first hands the other its contribution to the other's blocks, already
+  // Stream 0 writes columns 0..255 of the wave pair's rows (column blocks 0..7), stream 1 columns
+  // 256..511.  Each stream first hands the other its contribution to the other's blocks, already
   // weighted (a_s / l) and rounded to fp16 (2^-12 of that contribution, far below the bf16 output's
   // own rounding), through LDS; one barrier; then each adds what it received to its own weighted
-  // accumulators.  The fp16 rows meet in one staging area per wave pair, and each stream stores 32
-  // of its 64 rows.  (An fp32 hand-over of the raw accumulators, in two halves with a barrier
-  // each, moved twice the bytes through LDS.)
-  lds_char* stage = smem + (w & 1) * kStageBytes;
-  constexpr int kDumpBytes = 2 * 8 * 64 * 16;  // per wave: 2 groups x 8 (block, quad) x 64 lanes x 16 B
-  static_assert(2 * kStageBytes + kWaves * kDumpBytes <= kRing * kTileBytes, "staging and hand-over fit the ring");
-  lds_char* dump_mine = smem + 2 * kStageBytes + w * kDumpBytes;
-  const lds_char* dump_other = smem + 2 * kStageBytes + (w ^ 2) * kDumpBytes;
+  // accumulators, stages its 32 rows x 256 columns as fp16 rows and stores them.
+  constexpr int kStageRows2s = kRowsPerWave;
+  constexpr int kStageBytes2s = kStageRows2s * kStageRowBytes;
+  constexpr int kDumpBytes = 16 * 64 * 16;  // per wave: 16 x (two (block, quad) f16x4) x 64 lanes x 16 B
+  static_assert(kWaves * (kStageBytes2s + kDumpBytes) <= kRing * kTileBytes, "staging and hand-over fit the ring");
+  lds_char* stage = smem + w * kStageBytes2s;
+  lds_char* dump_mine = smem + kWaves * kStageBytes2s + w * kDumpBytes;
+  const lds_char* dump_other = smem + kWaves * kStageBytes2s + (w ^ 2) * kDumpBytes;
   // O = (O_0 a_0 + O_1 a_1) / l, with the division folded into the weights; a stream weighs its
-  // own accumulators with *_mine for its own blocks and for the blocks it hands over alike
-  const float own_mine = (stream == 0 ? co.a0 : co.a1) * co.inv;
-  const float par_mine = (stream == 0 ? cp.a0 : cp.a1) * cp.inv;
-  auto give = [&](auto ph_c, auto stream_c) __attribute__((always_inline)) {
-    constexpr int ph = decltype(ph_c)::value, S = decltype(stream_c)::value;
-    constexpr int gb = 4 * ph + (S == 0 ? 2 : 0);
+  // own accumulators with `mine` for its own blocks and for the blocks it hands over alike
+  const float mine = (stream == 0 ? co.a0 : co.a1) * co.inv;
+  auto weighted = [&](int b, int q4) {  // column block b, quad q4 of the lane: 4 weighted fp16 values
+    f16x4 v;
 #pragma unroll
-    for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const f32x16& oo = o_own[gb + cc];
-        const f32x16& op = o_par[gb + cc];
-        f16x4 vo, vp;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          vo[e] = (_Float16)(acc_read(oo[4 * q4 + e]) * own_mine);
-          vp[e] = (_Float16)(acc_read(op[4 * q4 + e]) * par_mine);
-        }
-        const i32x4 both = __builtin_shufflevector(__builtin_bit_cast(i32x2, vo), __builtin_bit_cast(i32x2, vp), 0, 1, 2, 3);
-        *(__attribute__((address_space(3))) i32x4*)(dump_mine + ((ph * 8 + cc * 4 + q4) * 64 + lane) * 16) = both;
-      }
+    for (int e = 0; e < 4; ++e) v[e] = (_Float16)(acc_read(o_acc[b][4 * q4 + e]) * mine);
+    return v;
   };
-  auto keep = [&](auto ph_c, auto stream_c, const i32x4 (&dd)[16]) __attribute__((always_inline)) {
-    constexpr int ph = decltype(ph_c)::value, S = decltype(stream_c)::value;
-    constexpr int kb = 4 * ph + (S == 0 ? 0 : 2);
+  // (the blocks a wave hands over and keeps depend on its stream: a wave-uniform branch picks one
+  // of two instantiations, so every accumulator index stays a compile-time constant)
+  auto give = [&](auto b0_c) __attribute__((always_inline)) {
+    constexpr int b0 = decltype(b0_c)::value;
 #pragma unroll
-    for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const f32x16& oo = o_own[kb + cc];
-        const f32x16& op = o_par[kb + cc];
-        const i32x4 d = dd[ph * 8 + cc * 4 + q4];
-        const f16x4 ro = __builtin_bit_cast(f16x4, (i32x2){d[0], d[1]});
-        const f16x4 rp = __builtin_bit_cast(f16x4, (i32x2){d[2], d[3]});
-        const int cb = (32 * (kb + cc) + 8 * q4 + 4 * hi) * 2;
-        f16x4 vo, vp;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          vo[e] = (_Float16)(acc_read(oo[4 * q4 + e]) * own_mine + (float)ro[e]);
-          vp[e] = (_Float16)(acc_read(op[4 * q4 + e]) * par_mine + (float)rp[e]);
-        }
-        *(__attribute__((address_space(3))) f16x4*)(stage + lrow * kStageRowBytes + cb) = vo;
-        *(__attribute__((address_space(3))) f16x4*)(stage + (32 + lrow) * kStageRowBytes + cb) = vp;
-      }
+    for (int jj = 0; jj < 16; ++jj) {  // (block, quad) pairs 2jj, 2jj + 1 of the 32 handed over
+      const int v0 = 2 * jj, v1 = 2 * jj + 1;
+      const f16x4 a = weighted(b0 + (v0 >> 2), v0 & 3), b = weighted(b0 + (v1 >> 2), v1 & 3);
+      *(__attribute__((address_space(3))) i32x4*)(dump_mine + (jj * 64 + lane) * 16) =
+          __builtin_shufflevector(__builtin_bit_cast(i32x2, a), __builtin_bit_cast(i32x2, b), 0, 1, 2, 3);
+    }
   };
-  if (stream == 0) {
-    give(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
-    give(std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{});
-  } else {
-    give(std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{});
-    give(std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{});
-  }
+  auto keep = [&](auto b0_c, const i32x4 (&dd)[16]) __attribute__((always_inline)) {
+    constexpr int b0 = decltype(b0_c)::value;
+#pragma unroll
+    for (int v = 0; v < 32; ++v) {
+      const int b = b0 + (v >> 2), q4 = v & 3;
+      const i32x4 d = dd[v >> 1];
+      const f16x4 r = __builtin_bit_cast(f16x4, (v & 1) ? (i32x2){d[2], d[3]} : (i32x2){d[0], d[1]});
+      f16x4 o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = (_Float16)(acc_read(o_acc[b][4 * q4 + e]) * mine + (float)r[e]);
+      const int cb = (32 * (v >> 2) + 8 * q4 + 4 * hi) * 2;  // byte column within the stream's 256
+      *(__attribute__((address_space(3))) f16x4*)(stage + lrow * kStageRowBytes + cb) = o;
+    }
+  };
+  if (stream == 0) give(std::integral_constant<int, kColBlocks / 2>{});
+  else give(std::integral_constant<int, 0>{});
   __syncthreads();  // both streams' hand-overs are in LDS
   {
     i32x4 dd[16];  // all reads go out before any is used
 #pragma unroll
     for (int j = 0; j < 16; ++j) dd[j] = *(const __attribute__((address_space(3))) i32x4*)(dump_other + (j * 64 + lane) * 16);
     __builtin_amdgcn_sched_barrier(0);
-    if (stream == 0) {
-      keep(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, dd);
-      keep(std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{}, dd);
-    } else {
-      keep(std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{}, dd);
-      keep(std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{}, dd);
-    }
+    if (stream == 0) keep(std::integral_constant<int, 0>{}, dd);
+    else keep(std::integral_constant<int, kColBlocks / 2>{}, dd);
   }
-  __syncthreads();  // both streams' columns are staged
   {
-    // stage rows 0..31 are wave pair h's own rows, 32..63 its partner's; stream s stores rows
-    // 32s .. 32s+31, two rows per store instruction
-    uint16_t* part_base = p.o_part + (int64_t)wi.bs * p.rows_pad * kDv + (w_uniform & 1) * (kDv / 2) + (lane & 31) * 8;
-    const int rbase = 32 * (w_uniform >> 1);
+    // the wave's 32 staged rows (rows 32*half ..), two rows per store instruction; the wave reads
+    // back only what it staged itself, so no barrier is needed here
+    uint16_t* part_base = p.o_part + (int64_t)wi.bs * p.rows_pad * kDv + (w_uniform >> 1) * (kDv / 2) + (lane & 31) * 8;
     i32x4 sv[16];  // all staged rows read first, then all stores
 #pragma unroll
     for (int k = 0; k < 16; ++k)
-      sv[k] = *(const __attribute__((address_space(3))) i32x4*)(stage + (rbase + 2 * k + hi) * kStageRowBytes + (lane & 31) * 16);
+      sv[k] = *(const __attribute__((address_space(3))) i32x4*)(stage + (2 * k + hi) * kStageRowBytes + (lane & 31) * 16);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
-      const int r = rbase + 2 * k + hi;
-      const int grow = row0 + (r < 32 ? half * kRowsPerWave + r : (1 - half) * kRowsPerWave + r - 32);
+      const int grow = row0 + half * kRowsPerWave + 2 * k + hi;
       if (grow < R) store16_through(part_base + (int64_t)grow * kDv, sv[k]);
     }
   }
@@ -1415,6 +1393,8 @@ void mla_verify_partial_2s(MLAV_LEAD_ARGS, PartialArgs args) {
   }
 }
 
+// Eight consecutive partial values: loaded raw (so that a batch of loads is in flight at
+// once), widened to fp32 when used.
 template <typename PartT>
 struct Raw8;
 template <>
