@@ -1411,10 +1411,10 @@ struct Raw8<_Float16> {
 };
 
 // kRowsPerBlock > 1 (with one split group): one wave per row, kRowsPerBlock consecutive rows of a
-// request per workgroup.  That is the form for the range plan, whose requests have few partials
-// each: a row's work is then one wave's few loads, and the plan (partials per request, request
-// offsets) is derived once per wave.
-template <typename PartT, int kMergeGroups, int kRowsPerBlock = 1>
+// request per workgroup.  kRanges: the partials come from the range plan, whose requests have few
+// partials each, so a row's work is one wave's few loads; the plan (the request's partial count
+// and output offset) is derived once per workgroup, by its first wave.
+template <typename PartT, int kMergeGroups, int kRowsPerBlock = 1, bool kRanges = false>
 __global__ __launch_bounds__(64 * kMergeGroups * kRowsPerBlock) void mla_verify_merge_kernel(MergeArgs p) {
   static_assert(kMergeGroups == 1 || kRowsPerBlock == 1, "several rows per workgroup take one split group each");
   __shared__ float group_sum[kMergeGroups > 1 ? kMergeGroups - 1 : 1][64][8];
@@ -1423,16 +1423,26 @@ __global__ __launch_bounds__(64 * kMergeGroups * kRowsPerBlock) void mla_verify_
   const int blocks_per_b = (rows_per_b + kRowsPerBlock - 1) / kRowsPerBlock;
   const int b = (int)(blockIdx.x / blocks_per_b);
   const int r = (int)(blockIdx.x - (int64_t)b * blocks_per_b) * kRowsPerBlock + (kRowsPerBlock > 1 ? tid >> 6 : 0);
-  if (b >= p.batch) return;
+  if (b >= p.batch) return;  // (uniform over the workgroup)
   int ns;
   int64_t qo = 0;
-  if (p.plan_ranges) {
-    const RequestScan rq = scan_requests(p.seq_lens, p.q_lens, p.batch, p.max_q_len, p.debug_flags);
-    if (r >= __builtin_amdgcn_readlane(rq.Q, b) * p.heads) return;
-    const int C = range_chunk(rq, p.nsplit, p.workers, p.min_tiles);
-    const int J = __builtin_amdgcn_readlane(rq.J, b), tiles = __builtin_amdgcn_readlane(rq.tiles, b);
-    ns = (J + tiles - 1) / C - J / C + 1;  // (tiles > 0: the request has rows)
-    qo = __builtin_amdgcn_readlane(rq.qo, b);
+  if constexpr (kRanges) {
+    __shared__ int plan[3];  // the request's partial count, first output row, rows
+    if (tid < 64) {
+      const RequestScan rq = scan_requests(p.seq_lens, p.q_lens, p.batch, p.max_q_len, p.debug_flags);
+      const int C = range_chunk(rq, p.nsplit, p.workers, p.min_tiles);
+      const int J = __builtin_amdgcn_readlane(rq.J, b), tiles = __builtin_amdgcn_readlane(rq.tiles, b);
+      const int qo_b = __builtin_amdgcn_readlane(rq.qo, b), rows_b = __builtin_amdgcn_readlane(rq.Q, b) * p.heads;
+      if (lane == 0) {
+        plan[0] = tiles > 0 ? (J + tiles - 1) / C - J / C + 1 : 0;
+        plan[1] = qo_b;
+        plan[2] = rows_b;
+      }
+    }
+    __syncthreads();
+    if (r >= plan[2]) return;  // (no barrier follows)
+    ns = plan[0];
+    qo = plan[1];
   } else {
     const int Q = clamped_q(p.q_lens, p.seq_lens, b, p.max_q_len, p.debug_flags);
     if (r >= Q * p.heads) return;
@@ -1644,9 +1654,17 @@ hipError_t launch_merge(const MergeArgs& a, hipStream_t stream) {
   const int64_t rows = (int64_t)a.batch * a.max_q_len * a.heads;  // one workgroup per row below
   const bool few = rows < kMergeFewRows && a.nsplit >= kMergeManySplits;
   // The library's fp16 partials with at most kMergeWaveSplits per row (the range plan, or a call such
-  // as ctx64k's 32 splits): one wave per row, four rows per workgroup.  At ctx64k this took 0.7 us
-  // less per call than 256 threads per row, measured on one box.
-  if (a.plan_ranges || (!a.part_fp32 && !few && a.nsplit <= kMergeWaveSplits)) {
+  // as ctx64k's 32 splits): one wave per row, four rows per workgroup (at ctx64k this took 0.7 us
+  // less per call than 256 threads per row, measured on one box); after the range plan 16 rows per
+  // workgroup, for which the plan is derived once.
+  if (a.plan_ranges) {
+    constexpr int kRowsPerBlock = 16;
+    const int64_t blocks = (int64_t)a.batch * ((a.max_q_len * a.heads + kRowsPerBlock - 1) / kRowsPerBlock);
+    hipLaunchKernelGGL((mla_verify_merge_kernel<_Float16, 1, kRowsPerBlock, true>), dim3((unsigned)blocks),
+                       dim3(64 * kRowsPerBlock), 0, stream, a);
+    return hipGetLastError();
+  }
+  if (!a.part_fp32 && !few && a.nsplit <= kMergeWaveSplits) {
     constexpr int kRowsPerBlock = 4;
     const int64_t blocks = (int64_t)a.batch * ((a.max_q_len * a.heads + kRowsPerBlock - 1) / kRowsPerBlock);
     hipLaunchKernelGGL((mla_verify_merge_kernel<_Float16, 1, kRowsPerBlock>), dim3((unsigned)blocks),
