@@ -98,6 +98,30 @@ def test_short_requests_whole_tensor(api, seed, lens, qlens, heads, nsplit, form
     _check(api, x, nsplit, f"short{seed} L={lens[0]} Q={qlens[0]} H={heads}", form)
 
 
+# Random batches, drawn once from a fixed generator: 1..8 requests with lengths 1..2,500 (ragged
+# last tiles, requests shorter than their draft block), 0..16 draft tokens each, 1..128 heads,
+# 1..48 splits, and each kernel-1 form (0: the library's choice, including the range plan for
+# batches of 2..64 requests).  Whole out and lse tensors against the oracle.
+def _random_batch_cases():
+    rng = np.random.default_rng(7777)
+    cases = []
+    for i in range(16):
+        B = int(rng.integers(1, 9))
+        lens = [int(v) for v in rng.integers(1, 2501, B)]
+        qlens = [int(min(L, rng.integers(0, 17))) for L in lens]
+        if max(qlens) == 0:
+            qlens[0] = 1
+        cases.append((500 + i, lens, qlens, int(rng.choice([1, 3, 16, 48, 64, 128])),
+                      int(rng.choice([1, 2, 3, 5, 8, 16, 32, 48])), int(rng.choice([0, 1, 2]))))
+    return cases
+
+
+@pytest.mark.parametrize("seed,lens,qlens,heads,nsplit,form", _random_batch_cases())
+def test_random_batches_whole_tensor(api, seed, lens, qlens, heads, nsplit, form):
+    x = I.make_custom(np.random.default_rng(seed), lens, qlens, heads, 2 * int(sum(lens)) + 64)
+    _check(api, x, nsplit, f"batch{seed} B={len(lens)} H={heads}", form)
+
+
 def test_ctx4k_workload(api):
     _check(api, I.make_inputs("ctx4k"), 8, "ctx4k")
 
