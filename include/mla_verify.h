@@ -85,7 +85,8 @@ typedef struct {
 
 /* Kernel-1 layouts (the result is the same up to rounding; they differ in speed).
  * 128ROW: workgroups of 128 (draft token, head) rows, one 32-key tile per step.
- * TWO_STREAM: workgroups of 64 rows over two key streams (two tiles per step).
+ * TWO_STREAM: workgroups of 64 rows over two key streams (two tiles per step);
+ *   each wave's P.V covers its own 32 rows over all 512 output columns.
  * AUTO: TWO_STREAM for requests of at most 64 rows, and for calls whose 128-row
  * workgroups (B * nsplit * ceil(Q_max*H/128)) would occupy at most half of the
  * CUs; 128ROW otherwise.  Batches of 2..64 requests in the 128-row form spread
@@ -98,7 +99,8 @@ typedef struct {
 /*
  * Validate `cfg`, allocate the split workspace on the current device
  * (B * max_nsplit * ceil(Q_max*H/128)*128 rows of 512 fp16 partial outputs,
- * each normalised within its split, plus one fp32 log-sum-exp each) and
+ * 64 rows per split instead when Q_max*H <= 64, each normalised within its
+ * split, plus one fp32 log-sum-exp each) and
  * return a handle in *out.  Call outside graph capture.
  * Errors: INVALID_ARGUMENT (null, non-positive sizes, unknown form or flag), UNSUPPORTED (dims),
  * OUT_OF_MEMORY, HIP (no device).  On error *out is set to NULL.
