@@ -1217,6 +1217,8 @@ void mla_verify_partial_2s(MLAV_LEAD_ARGS, PartialArgs args) {
       for (int ks = 0; ks < kQkSteps; ++ks) {
         __builtin_amdgcn_sched_barrier(0);
         if (ks + kPrefetch < kQkSteps) kread(tb, ks + kPrefetch);
+        // the first V^T fragments of the tile, for the P.V after the softmax
+        if (ks >= kQkSteps - kVPrefetch) vread(tb, ks - (kQkSteps - kVPrefetch));
         __builtin_amdgcn_sched_barrier(0);
         if (ks == 0) mfma_first_v(sacc, kf[ks], qf[ks]);
         else mfma_acc_v(sacc, kf[ks], qf[ks]);
@@ -1235,10 +1237,8 @@ void mla_verify_partial_2s(MLAV_LEAD_ARGS, PartialArgs args) {
         st.m_ref = tile_row_max(sacc) * p.scale_log2 + kRefHeadroom;
         nmref = (st.m_ref == -INFINITY) ? 0.f : -st.m_ref;
       }
-      // The first V^T fragments go out now and land during the first half of the softmax: the
-      // lane's scores 0..7 (keys 0..15 of the tile, what the first 16 P.V MFMAs take)
-#pragma unroll
-      for (int n = 0; n < kVPrefetch; ++n) vread(tb, n);
+      // the first half of the softmax: the lane's scores 0..7 (keys 0..15 of the tile, what the
+      // first 16 P.V MFMAs take)
 #pragma unroll
       for (int j = 0; j < 8; ++j) sm.s[j] = vfma(sacc[j], p.scale_log2, nmref);
 #pragma unroll
