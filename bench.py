@@ -131,6 +131,20 @@ def _graph_us(torch, fn, reps=10, rounds=20):
     return statistics.median(a.elapsed_time(b) * 1e3 / reps for a, b in ev)
 
 
+def kernel1_name(w, x, nsplit, form, cus):
+    """The kernel-1 form a call takes (include/mla_verify.h, MLA_VERIFY_FORM_*): a fixed `form`, or
+    the library's choice for FORM_AUTO (0)."""
+    names = {1: "mla_verify_partial", 2: "mla_verify_partial_2s", 3: "mla_verify_partial_4s"}
+    if form:
+        return names[form]
+    req_rows = x.heads * int(x.q_lens.max())
+    range_plan = req_rows > 64 and 2 <= w.batch <= 64
+    two_stream = req_rows <= 64 or (not range_plan and 2 * w.batch * nsplit * -(-req_rows // 128) <= cus)
+    if two_stream and 2 * w.batch * nsplit * -(-req_rows // 64) <= cus:
+        return names[3]
+    return names[2] if two_stream else names[1]
+
+
 def bench_compact(args, w, x, h, q, pool, slot_idx, seq_lens, q_lens, out, lse, nsplit):
     """KV compaction of every row the workload references into a fresh contiguous buffer (one
     launch, HBM-bound: each 1152-B row read once and written once), then kernel 1 and the whole
@@ -336,6 +350,8 @@ def main():
                     help="seconds of untimed back-to-back calls before the timed region (besides --warmup)")
     ap.add_argument("--workload", default="ctx64k")
     ap.add_argument("--nsplit", type=int, default=None)
+    ap.add_argument("--form", type=int, default=0, choices=[0, 1, 2, 3],
+                    help="kernel-1 layout: 0 the library's choice, 1 128-row, 2 two-stream, 3 four-stream")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold", type=int, default=50, help="single-call replays, each after reading 1 GiB to flush the caches")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for the CPU baseline")
@@ -394,7 +410,7 @@ def main():
     t_q = x.q.shape[0]
     out = torch.empty((t_q, x.heads, I.D_V), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((t_q, x.heads), dtype=torch.float32, device=dev)
-    h = api.MlaVerify(x.heads, w.batch, int(x.q_lens.max()), nsplit, x.num_slots, x.scale)
+    h = api.MlaVerify(x.heads, w.batch, int(x.q_lens.max()), nsplit, x.num_slots, x.scale, form=args.form)
     step = lambda: h.run(q, pool, slot_idx, seq_lens, q_lens, out, lse, nsplit)  # noqa: E731
     part = lambda: h.partials(q, pool, slot_idx, seq_lens, q_lens, nsplit)  # noqa: E731
     if args.compact:
@@ -542,12 +558,7 @@ def main():
     # kernel 1's roof: bf16 MFMA above the ridge (flop per byte of the call's algorithmic bytes),
     # HBM below it (q_len = 1 decode: H flop/B ~ 121 against a ridge of 312)
     ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBPS * 1e9)
-    # the kernel-1 form the library picks (include/mla_verify.h, MLA_VERIFY_FORM_AUTO)
-    req_rows = x.heads * int(x.q_lens.max())
-    range_plan = req_rows > 64 and 2 <= w.batch <= 64
-    two_stream = req_rows <= 64 or (not range_plan and 2 * w.batch * nsplit * -(-req_rows // 128)
-                                    <= torch.cuda.get_device_properties(0).multi_processor_count)
-    k1_kernel = "mla_verify_partial_2s" if two_stream else "mla_verify_partial"
+    k1_kernel = kernel1_name(w, x, nsplit, args.form, torch.cuda.get_device_properties(0).multi_processor_count)
     # `achieved`/`frac` are the dominant kernel's (kernel 1: all of the call's FLOPs, and its KV
     # stream); `call_achieved`/`call_frac` hold the whole captured call (kernel 1, the merge and the
     # gap between them) against the same roof.

@@ -70,7 +70,8 @@ typedef struct {
   int32_t max_nsplit; /* >= 1: the workspace holds this many partials per row */
   int64_t num_slots;  /* rows in kv_pool (>= 1) */
   float sm_scale;     /* score scale, > 0 (1/sqrt(192) in the reference workloads) */
-  int32_t form;       /* kernel-1 layout: MLA_VERIFY_FORM_AUTO (0), _128ROW (1) or _TWO_STREAM (2) */
+  int32_t form;       /* kernel-1 layout: MLA_VERIFY_FORM_AUTO (0), _128ROW (1), _TWO_STREAM (2) or
+                         _FOUR_STREAM (3) */
   int32_t flags;      /* OR of MLA_VERIFY_FLAG_* (0: none) */
 } mla_verify_config;
 
@@ -87,14 +88,19 @@ typedef struct {
  * 128ROW: workgroups of 128 (draft token, head) rows, one 32-key tile per step.
  * TWO_STREAM: workgroups of 64 rows over two key streams (two tiles per step);
  *   each wave's P.V covers its own 32 rows over all 512 output columns.
+ * FOUR_STREAM: workgroups of 32 rows over four key streams, one per wave, in
+ *   16-key half tiles (Q.K on MFMA 16x16x32); no barrier in the step loop.
  * AUTO: TWO_STREAM for requests of at most 64 rows, and for calls whose 128-row
  * workgroups (B * nsplit * ceil(Q_max*H/128)) would occupy at most half of the
- * CUs; 128ROW otherwise.  Batches of 2..64 requests in the 128-row form spread
- * their keys over the CUs by the range plan (see mla_verify_run).  Use a fixed
- * form to compare or test the layouts. */
+ * CUs; 128ROW otherwise; then FOUR_STREAM instead of TWO_STREAM for calls whose
+ * 64-row workgroups (B * nsplit * ceil(Q_max*H/64)) would occupy at most half of
+ * the CUs.  Batches of 2..64 requests in the 128-row form spread their keys over
+ * the CUs by the range plan (see mla_verify_run).  Use a fixed form to compare or
+ * test the layouts. */
 #define MLA_VERIFY_FORM_AUTO 0
 #define MLA_VERIFY_FORM_128ROW 1
 #define MLA_VERIFY_FORM_TWO_STREAM 2
+#define MLA_VERIFY_FORM_FOUR_STREAM 3
 
 /*
  * Validate `cfg`, allocate the split workspace on the current device

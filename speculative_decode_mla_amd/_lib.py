@@ -25,6 +25,7 @@ NOALLOC_SCRATCH_BYTES = 40 << 20  # MLA_VERIFY_NOALLOC_SCRATCH_BYTES
 FORM_AUTO = 0        # kernel-1 layouts (include/mla_verify.h)
 FORM_128ROW = 1
 FORM_TWO_STREAM = 2
+FORM_FOUR_STREAM = 3
 FLAG_BATCH_INVARIANT = 1  # create flags (include/mla_verify.h)
 
 D_QK = 576

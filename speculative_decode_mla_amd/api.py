@@ -45,8 +45,8 @@ class MlaVerify:
 
     run() enqueues the two kernels on the current (or given) stream and returns
     without synchronising, so it can be captured in a torch.cuda.CUDAGraph.
-    `form` picks kernel 1's layout (FORM_AUTO, FORM_128ROW or FORM_TWO_STREAM from
-    _lib); the result is the same up to rounding, only the speed differs.
+    `form` picks kernel 1's layout (FORM_AUTO, FORM_128ROW, FORM_TWO_STREAM or FORM_FOUR_STREAM
+    from _lib); the result is the same up to rounding, only the speed differs.
     `batch_invariant` makes each request's result bitwise independent of its batchmates
     (MLA_VERIFY_FLAG_BATCH_INVARIANT: no range plan).  `debug` runs the handle on the debug build
     of the library, whose kernels clamp out-of-range slots and lengths and record them

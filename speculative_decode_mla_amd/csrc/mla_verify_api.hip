@@ -45,32 +45,40 @@ int validate_config(const mla_verify_config* cfg) {
   if (!(cfg->sm_scale > 0.f) || !std::isfinite(cfg->sm_scale)) return MLA_ERR_INVALID_ARGUMENT;
   if (cfg->d_qk != MLA_VERIFY_D_QK || cfg->d_v != MLA_VERIFY_D_V) return MLA_ERR_UNSUPPORTED;
   if (cfg->form != MLA_VERIFY_FORM_AUTO && cfg->form != MLA_VERIFY_FORM_128ROW &&
-      cfg->form != MLA_VERIFY_FORM_TWO_STREAM)
+      cfg->form != MLA_VERIFY_FORM_TWO_STREAM && cfg->form != MLA_VERIFY_FORM_FOUR_STREAM)
     return MLA_ERR_INVALID_ARGUMENT;
   if ((cfg->flags & ~MLA_VERIFY_FLAG_BATCH_INVARIANT) != 0) return MLA_ERR_INVALID_ARGUMENT;
   const int64_t rows = (int64_t)cfg->max_q_len * cfg->num_heads;
-  const int64_t grid = (int64_t)cfg->batch * cfg->max_nsplit * ((rows + mlav::kRowsPerGroup2s - 1) / mlav::kRowsPerGroup2s);
+  const int64_t grid = (int64_t)cfg->batch * cfg->max_nsplit * ((rows + mlav::kRowsPerGroup4s - 1) / mlav::kRowsPerGroup4s);
   if (rows > INT32_MAX / 2 || grid > INT32_MAX || (int64_t)cfg->batch * rows > INT32_MAX)
     return MLA_ERR_INVALID_ARGUMENT;
   return MLA_OK;
 }
 
-// Kernel-1 form of a config before the per-call choice: 1 (128-row workgroups) or 2 (two streams).
+// Kernel-1 form of a config before the per-call choice: 1 (128-row workgroups), 2 (two streams) or
+// 4 (four streams).
 int32_t config_streams(const mla_verify_config* cfg) {
   const int64_t rows = (int64_t)cfg->max_q_len * cfg->num_heads;
   // Requests of at most 64 rows (a q_len = 1 decode step with H <= 64) use the two-stream form of
-  // kernel 1, whose workgroups hold 64 rows; larger ones the 128-row form (or, per call, the
-  // two-stream form when the 128-row workgroups would leave most CUs idle; see launch_partials).
-  return cfg->form == MLA_VERIFY_FORM_TWO_STREAM ? 2
-         : cfg->form == MLA_VERIFY_FORM_128ROW   ? 1
-         : rows <= mlav::kRowsPerGroup2s        ? 2 : 1;
+  // kernel 1, whose workgroups hold 64 rows; larger ones the 128-row form (or, per call, a form of
+  // fewer rows per workgroup when the call's workgroups would leave most CUs idle; see
+  // launch_partials).
+  return cfg->form == MLA_VERIFY_FORM_FOUR_STREAM ? 4
+         : cfg->form == MLA_VERIFY_FORM_TWO_STREAM ? 2
+         : cfg->form == MLA_VERIFY_FORM_128ROW     ? 1
+         : rows <= mlav::kRowsPerGroup2s          ? 2 : 1;
+}
+
+// Rows per workgroup of a kernel-1 form.
+int64_t form_rows(int32_t streams) {
+  return streams == 4 ? mlav::kRowsPerGroup4s : streams == 2 ? mlav::kRowsPerGroup2s : mlav::kRowsPerGroup;
 }
 
 // Workspace rows per partial: rows past 64 are padded to a multiple of 128, which holds the row
-// groups of either form.
+// groups of any form.
 int64_t config_rows_pad(const mla_verify_config* cfg) {
   const int64_t rows = (int64_t)cfg->max_q_len * cfg->num_heads;
-  const int64_t group = config_streams(cfg) == 2 ? mlav::kRowsPerGroup2s : mlav::kRowsPerGroup;
+  const int64_t group = config_streams(cfg) == 1 ? mlav::kRowsPerGroup : mlav::kRowsPerGroup2s;
   return rows <= mlav::kRowsPerGroup2s ? (rows + group - 1) / group * group
                                        : (rows + mlav::kRowsPerGroup - 1) / mlav::kRowsPerGroup * mlav::kRowsPerGroup;
 }
@@ -80,7 +88,7 @@ int64_t config_rows_pad(const mla_verify_config* cfg) {
 void fill_geometry(const mla_verify_config* cfg, int dev, int cus, mla_verify_s* h) {
   const int64_t rows = (int64_t)cfg->max_q_len * cfg->num_heads;
   const int32_t streams = config_streams(cfg);
-  const int64_t group = streams == 2 ? mlav::kRowsPerGroup2s : mlav::kRowsPerGroup;
+  const int64_t group = form_rows(streams);
   const int64_t row_groups = (rows + group - 1) / group;
   h->cfg = *cfg;
   h->device = dev;
@@ -201,6 +209,13 @@ int launch_partials(mla_verify_handle h, const void* q, const void* kv_pool, con
       2 * form_batch * nsplit * h->row_groups <= h->cus) {
     pa.streams = 2;
     pa.row_groups = (h->rows + mlav::kRowsPerGroup2s - 1) / mlav::kRowsPerGroup2s;  // rows_pad (a multiple of 128) holds them
+  }
+  // In the same way, a call whose 64-row workgroups would occupy at most half of the CUs (a short
+  // context with few splits, a decode step with few splits) takes the four-stream form: 32-row
+  // workgroups, twice as many again.
+  if (c.form == MLA_VERIFY_FORM_AUTO && pa.streams == 2 && 2 * form_batch * nsplit * pa.row_groups <= h->cus) {
+    pa.streams = 4;
+    pa.row_groups = (h->rows + mlav::kRowsPerGroup4s - 1) / mlav::kRowsPerGroup4s;
   }
   pa.plan_ranges = h->plan_ranges;
   pa.workers = h->workers;

@@ -15,6 +15,7 @@ constexpr int kRowsPerWave = 32;     // (token, head) rows owned by one wave
 constexpr int kRowsPerGroup = kWaves * kRowsPerWave;  // rows per workgroup: 128
 constexpr int kTileKeys = 32;        // keys gathered into LDS per step (one MFMA block)
 constexpr int kRowsPerGroup2s = 2 * kRowsPerWave;  // rows per workgroup in the two-stream form: 64
+constexpr int kRowsPerGroup4s = kRowsPerWave;      // rows per workgroup in the four-stream form: 32
 constexpr int kRangeMaxBatch = 64;   // the range plan holds one request per lane of a wave
 
 // Kernel 1: one workgroup per (request, split, 128-row group).
@@ -27,10 +28,11 @@ struct PartialArgs {
   uint16_t* o_part;          // fp16 [B, nsplit, rows_pad, 512], each row normalised within its split
   float* lse_part;           // fp32 [B, nsplit, rows_pad], natural log
   int32_t batch, heads, max_q_len, nsplit;
-  int32_t row_groups;        // ceil(max_q_len*H / 128)
-  int32_t rows_pad;          // row_groups * 128
+  int32_t row_groups;        // ceil(max_q_len*H / rows per workgroup of the form)
+  int32_t rows_pad;          // workspace rows per partial (at least max_q_len*H)
   int32_t min_tiles;         // fewest 32-key tiles a split is given (caps the split count)
-  int32_t streams;           // 1: 128-row workgroups; 2: 64-row workgroups over two key streams
+  int32_t streams;           // 1: 128-row workgroups; 2: 64-row workgroups over two key streams;
+                             // 4: 32-row workgroups over four key streams
   int32_t plan_ranges;       // 1: range plan (128-row form, 2..kRangeMaxBatch requests); 0: splits per request
   int32_t workers;           // range plan: workers (each one workgroup per row group)
   float scale_log2;          // sm_scale * log2(e)

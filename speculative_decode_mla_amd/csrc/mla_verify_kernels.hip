@@ -152,6 +152,16 @@ __device__ __forceinline__ float pair_sum(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
+// ... and over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (one row of a 16x16 MFMA result); all four
+// lanes get the same bits
+__device__ __forceinline__ float quad_max(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return pair_max(fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
+}
+__device__ __forceinline__ float quad_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return pair_sum(__uint_as_float(r[0]) + __uint_as_float(r[1]));
+}
 
 // MFMA 32x32x16 bf16 issued through inline asm so that the accumulator stays in
 // the register class chosen here: the 256-register output accumulator in
@@ -173,6 +183,13 @@ __device__ __forceinline__ void mfma_acc_v(f32x16& acc, const bf16x8& a, const b
 }
 __device__ __forceinline__ void mfma_first_v(f32x16& acc, const bf16x8& a, const bf16x8& b) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(acc) : "v"(a), "v"(b));
+}
+// MFMA 16x16x32 bf16 (the four-stream form's Q.K), accumulator in VGPRs
+__device__ __forceinline__ void mfma16_acc_v(f32x4& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma16_first_v(f32x4& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
 }
 
 // Single VALU ops as volatile statements, so that each stays in the MFMA gap it
@@ -1393,6 +1410,370 @@ void mla_verify_partial_2s(MLAV_LEAD_ARGS, PartialArgs args) {
   }
 }
 
+// ---- Kernel 1, four-stream form: 32-row workgroups ---------------------------------------------------
+// For calls whose two-stream grid would still leave at least half of the CUs idle (a short context
+// with few splits, a q_len = 1 decode step with few splits): the four waves hold the same 32 rows and
+// run four key streams over the split, in 16-key half tiles, half tile j to wave j % 4.  Each wave
+// gathers, multiplies and accumulates its own half tiles in two half-tile buffers (keys 0..15 and
+// 16..31 of ring buffer w), so the step loop has no barrier.  At the end the four streams'
+// accumulators are combined through LDS, as in the two-stream form, into one partial per split.
+//   * Q.K on MFMA 16x16x32 bf16 as S^T = K . Q^T, one MFMA per 16-row half of the rows: the A
+//     operand (16 keys x 32 dims) comes from the half-tile buffer, the B operand (32 dims x 16 rows)
+//     is resident (36 fragments: 18 dim steps x 2 row halves).  In the C layout lane l holds keys
+//     4(l/16) .. 4(l/16) + 3 of row l % 16 (first half) and of row 16 + l % 16 (second half).
+//   * P.V as in the other forms (MFMA 32x32x16, O^T = V^T . P^T, one 16-key step per half tile).  A
+//     permlane16 swap and a permlane32 swap of the bf16-packed probabilities give lane l eight keys of
+//     row l % 32 in the key order of the 32x32 S^T layout's first 16-key step, which the V^T
+//     fragments already follow: keys 0-3, 8-11 in lanes 0..31 and 4-7, 12-15 in lanes 32..63.
+constexpr int kHalfTileBytes = 2 * kKeyBlockBytes;  // 16 keys
+constexpr int kQkSteps16 = kDqk / 32;               // 18 dim steps of MFMA 16x16x32
+static_assert(kQkSteps16 == 2 * kDmaPerTile, "one gather load per Q.K dim step");
+
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+void mla_verify_partial_4s(MLAV_LEAD_ARGS, PartialArgs args) {
+  PartialArgs p = args;
+  MLAV_LEAD_INTO(p);
+  __shared__ __attribute__((aligned(1024))) char smem_raw[kRing * kTileBytes + kXchgBytes];
+  lds_char* smem = (lds_char*)smem_raw;
+
+  WorkItem wi;
+  if (!decode_work(p, blockIdx.x, kRowsPerGroup4s, wi)) return;
+  const int L = wi.L, Q = wi.Q, H = p.heads, R = wi.R;
+  const int nh = 2 * (wi.t_end - wi.t_begin);  // 16-key half tiles of the split
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int w_uniform = __builtin_amdgcn_readfirstlane(w);
+  const int g4 = lane >> 4, c16 = lane & 15, hi = lane >> 5, lrow = lane & 31;
+  const int row0 = wi.g * kRowsPerGroup4s;
+  // Q.K layout: the lane's rows c16 (x) and 16 + c16 (y) of the group; rows past R use token 0
+  const int rx = row0 + c16, ry = row0 + 16 + c16;
+  const int limx = L - Q + (rx < R ? rx / H : 0) + 1;  // row x sees keys [0, limx)
+  const int limy = L - Q + (ry < R ? ry / H : 0) + 1;
+  const int mask_from = L - Q + 1;  // first key some draft row cannot see
+  const int nst = nh > w_uniform ? (nh - w_uniform + 3) / 4 : 0;  // this stream's half tiles
+
+  // ---- gather set-up: the wave moves both key blocks (keys 0..7, 8..15) of its half tile k (the
+  // split's half tile 4k + w) into half-buffer k & 1 of ring buffer w; keys past the request's end
+  // use its last key's row (scores masked) -------------------------------------------------------------
+  const int g_kr = lane >> 3;
+  const char* kv = (const char*)p.kv;
+  const uint32_t smem_base = (uint32_t)(uintptr_t)smem;
+  const int32_t* slots_g = p.slot_idx + wi.ko;
+  auto gather_key = [&](int k, int j) {
+    const int kk = k < nst ? k : (nst > 0 ? nst - 1 : 0);
+    const int key = (2 * wi.t_begin + 4 * kk + w_uniform) * 16 + 8 * j + g_kr;
+    return key < L ? key : L - 1;
+  };
+  auto g_row = [&](int slot, int j) { return kv + (int64_t)slot * kRowBytes + (((lane & 7) ^ g_kr ^ j) << 4); };
+  auto g_lds = [&](int k, int j) {
+    return smem_base + w_uniform * kTileBytes + (k & 1) * kHalfTileBytes + j * kKeyBlockBytes;
+  };
+
+  // Q.K operands of dim step ks (A: key c16 of a half-tile buffer; B: row c16 of a staged q half),
+  // 16-B chunk 4 ks + g4 in the tile layout: kaddr16[ks & 1] + (ks >> 1) * 1 KiB from the buffer
+  int kaddr16[2];
+  {
+    const int kr = c16 & 7, f = kr ^ (c16 >> 3);
+    const int base = (c16 >> 3) * kKeyBlockBytes + kr * 128;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) kaddr16[e] = base + (((4 * e + g4) ^ f) << 4);
+  }
+
+  // ---- prologue: slot indices of half tile 0; the q rows, staged as four key blocks (rows 8w ..
+  // 8w + 7 moved by wave w) in the upper half-buffers of ring buffers 2 (rows 0..15) and 3 (rows
+  // 16..31); half tile 0 of every stream (lower half-buffers) while they land.  Half tile 1 of
+  // streams 2 and 3 goes to those upper halves after the barrier that follows every wave's q reads.
+  int sl[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) sl[j] = load_b32_untracked(slots_g + gather_key(0, j));
+  static_assert(kDmaPerTile == 9, "wait counts below");
+  {
+    const uint32_t qblk =
+        smem_base + (2 + (w_uniform >> 1)) * kTileBytes + kHalfTileBytes + (w_uniform & 1) * kKeyBlockBytes;
+    const int r = row0 + 8 * w_uniform + g_kr;
+    const int64_t qrow = wi.qo * H + (r < R ? r : 0);
+    dma_key_block((const char*)(p.q + qrow * kDqk) + (((lane & 7) ^ g_kr ^ (w_uniform & 1)) << 4), qblk);
+  }
+  // the slot indices have landed (the 9 q loads issued after them may still be in flight)
+  asm volatile("s_waitcnt vmcnt(9)" : "+v"(sl[0]), "+v"(sl[1]) : : "memory");
+#pragma unroll
+  for (int j = 0; j < 2; ++j) sl[j] = checked_slot(sl[j], p.num_slots, p.debug_flags);
+  if (nst > 0) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) dma_key_block(g_row(sl[j], j), g_lds(0, j));
+    MLAV_WAIT_VMCNT(18);  // the q block has landed (half tile 0's 18 loads may still be in flight)
+  } else {
+    MLAV_WAIT_VMCNT(0);
+  }
+  __syncthreads();  // every wave's q block is visible
+  bf16x8 qf[2][kQkSteps16];
+#pragma unroll
+  for (int rh = 0; rh < 2; ++rh) {
+    const lds_char* qb = smem + (2 + rh) * kTileBytes + kHalfTileBytes;
+#pragma unroll
+    for (int ks = 0; ks < kQkSteps16; ++ks)
+      qf[rh][ks] = *(const __attribute__((address_space(3))) bf16x8*)(qb + kaddr16[ks & 1] + (ks >> 1) * kBlockBytes);
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
+  __syncthreads();  // every wave holds its q fragments: the upper halves of buffers 2 and 3 are free
+  int sn[2];  // slots of the next half tile to gather (compiler-tracked loads, awaited at the next step)
+#pragma unroll
+  for (int j = 0; j < 2; ++j) sn[j] = slots_g[gather_key(1, j)];
+
+  // P.V A operand addresses, as in the other forms (the column block's offset is added per read)
+  int vaddr[2][2];
+  {
+    const int G = lane >> 4, j = lane & 15;
+    const int kr = 4 * (G >> 1) + (j >> 2);
+    const int u = 2 * (G & 1) + ((j & 3) >> 1);
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+        vaddr[e][r] = r * kKeyBlockBytes + kr * 128 + (((4 * e) ^ u ^ kr ^ r) << 4) + (j & 1) * 8;
+  }
+  // O^T of the group's 32 rows over this stream's keys, all 512 columns
+  f32x16 o_acc[kColBlocks];
+#pragma unroll
+  for (int c = 0; c < kColBlocks; ++c) {
+    o_acc[c] = (f32x16){};
+    asm volatile("" : "+a"(o_acc[c]));  // zeroed here, in AGPRs (see the two-stream form)
+  }
+  // the stream's softmax state for rows x and y (the lane's share of the row sums)
+  float m_x = -INFINITY, m_y = -INFINITY, nm_x = 0.f, nm_y = 0.f;
+  float lr_x = 0.f, lr_y = 0.f, le_x = 0.f, le_y = 0.f;
+  bf16x8 kf[kQkSteps16];
+  auto kread = [&](const lds_char* hb, int ks) {
+    kf[ks] = *(const __attribute__((address_space(3))) bf16x8*)(hb + kaddr16[ks & 1] + (ks >> 1) * kBlockBytes);
+  };
+  bf16x8 vf[kColBlocks];  // V^T fragment of column block n over the half tile's 16 keys
+  auto vread = [&](const lds_char* hb, int n) {
+    const lds_char* vb = hb + (n >> 1) * kBlockBytes;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)(vb + vaddr[n & 1][0]));
+    const i16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)(vb + vaddr[n & 1][1]));
+    vf[n] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+
+  for (int k = 0; k < nst; ++k) {
+    const lds_char* hb = smem + w_uniform * kTileBytes + (k & 1) * kHalfTileBytes;
+    MLAV_WAIT_VMCNT(0);  // this wave's half tile k (and the slot loads for the next gather) have landed
+    const bool refill = k + 1 < nst;
+    const char* r0 = g_row(checked_slot(sn[0], p.num_slots, p.debug_flags), 0);
+    const char* r1 = g_row(checked_slot(sn[1], p.num_slots, p.debug_flags), 1);
+    if (refill) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) sn[j] = slots_g[gather_key(k + 2, j)];
+    }
+    const uint32_t l0 = g_lds(k + 1, 0), l1 = g_lds(k + 1, 1);
+    // Q.K of half tile k for both row halves, the gathers of half tile k + 1 between the MFMAs, the
+    // first V^T fragments in the last dim steps
+    f32x4 sx, sy;
+#pragma unroll
+    for (int ks = 0; ks < kPrefetch; ++ks) kread(hb, ks);
+#pragma unroll
+    for (int ks = 0; ks < kQkSteps16; ++ks) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (ks + kPrefetch < kQkSteps16) kread(hb, ks + kPrefetch);
+      if (ks >= kQkSteps16 - kVPrefetch) vread(hb, ks - (kQkSteps16 - kVPrefetch));
+      __builtin_amdgcn_sched_barrier(0);
+      if (ks == 0) {
+        mfma16_first_v(sx, kf[ks], qf[0][ks]);
+        mfma16_first_v(sy, kf[ks], qf[1][ks]);
+      } else {
+        mfma16_acc_v(sx, kf[ks], qf[0][ks]);
+        mfma16_acc_v(sy, kf[ks], qf[1][ks]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (refill) {
+        if (ks < kDmaPerTile) dma_chunk_group(r0, l0, ks);
+        else dma_chunk_group(r1, l1, ks - kDmaPerTile);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile(MLAV_MFMA_DRAIN : "+v"(sx), "+v"(sy));
+    const int key0 = (2 * wi.t_begin + 4 * k + w_uniform) * 16 + 4 * g4;  // the lane's first key
+    if (key0 - 4 * g4 + 16 > mask_from) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        sx[r] = key0 + r < limx ? sx[r] : -INFINITY;
+        sy[r] = key0 + r < limy ? sy[r] : -INFINITY;
+      }
+    }
+    if (k == 0) {  // the stream's references: the row maxima of its first half tile (see the 128-row form)
+      m_x = quad_max(fmaxf(fmaxf(sx[0], sx[1]), fmaxf(sx[2], sx[3]))) * p.scale_log2 + kRefHeadroom;
+      m_y = quad_max(fmaxf(fmaxf(sy[0], sy[1]), fmaxf(sy[2], sy[3]))) * p.scale_log2 + kRefHeadroom;
+      nm_x = (m_x == -INFINITY) ? 0.f : -m_x;
+      nm_y = (m_y == -INFINITY) ? 0.f : -m_y;
+    }
+    float ex[4], ey[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) ex[r] = vfma(sx[r], p.scale_log2, nm_x);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) ey[r] = vfma(sy[r], p.scale_log2, nm_y);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) ex[r] = vexp2(ex[r]);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) ey[r] = vexp2(ey[r]);
+    const int px0 = vpack_bf16(ex[0], ex[1]), px1 = vpack_bf16(ex[2], ex[3]);
+    const int py0 = vpack_bf16(ey[0], ey[1]), py1 = vpack_bf16(ey[2], ey[3]);
+    // lanes of rows 0..15 give their row 16.. keys to, and take their own row's next keys from, the
+    // lanes 16 above (permlane16), then the halves swap (permlane32): see the layout note above
+    const auto s0 = __builtin_amdgcn_permlane16_swap(px0, py0, false, false);
+    const auto s1 = __builtin_amdgcn_permlane16_swap(px1, py1, false, false);
+    const auto t0 = __builtin_amdgcn_permlane32_swap(s0[0], s0[1], false, false);
+    const auto t1 = __builtin_amdgcn_permlane32_swap(s1[0], s1[1], false, false);
+    i32x4 pv = (i32x4){(int)t0[0], (int)t1[0], (int)t0[1], (int)t1[1]};
+    // wait states between the swaps and the first MFMA reading their results (the operand ties the
+    // nop to the swaps, which the compiler would otherwise schedule past it)
+    asm volatile("s_nop 3" : "+v"(pv));
+    const bf16x8 pb = __builtin_bit_cast(bf16x8, pv);
+    // P.V over the 16 column blocks; the row sums between the MFMAs
+#pragma unroll
+    for (int n = 0; n < kColBlocks; ++n) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (n + kVPrefetch < kColBlocks) vread(hb, n + kVPrefetch);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_acc_a(o_acc[n], vf[n], pb);
+      __builtin_amdgcn_sched_barrier(0);
+      if (n < 4) vadd_to(le_x, ex[n]);
+      else if (n < 8) vadd_to(le_y, ey[n - 4]);
+      else if (n == 8) vsum_pair_to(lr_x, px0);
+      else if (n == 9) vsum_pair_to(lr_x, px1);
+      else if (n == 10) vsum_pair_to(lr_y, py0);
+      else if (n == 11) vsum_pair_to(lr_y, py1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  MLAV_WAIT_VMCNT(0);  // the last slot loads
+  // The accumulators are read below only through acc_read (volatile), which stays behind this drain.
+  asm volatile(MLAV_MFMA_DRAIN);
+
+  // ---- merge of the four streams, then the partial write.  With m = max_s m_s, a_s = 2^(m_s - m):
+  // l = sum_s a_s l_s and O = sum_s a_s O_s.  The per-row (m_s, l_s, l_exact_s) go through LDS; wave w
+  // writes column blocks 4w .. 4w + 3 and first hands every other wave its weighted contribution to
+  // that wave's blocks, rounded to fp16 (as in the two-stream form).  A row where any stream's sum
+  // outgrew its reference is redone exactly over the whole split.
+  const float ltx = quad_sum(lr_x), lty = quad_sum(lr_y);
+  const float lex = quad_sum(le_x), ley = quad_sum(le_y);
+  __syncthreads();  // every wave is done with the ring
+  float* stat = (float*)(smem_raw + kRing * kTileBytes);  // [wave][32 rows][3]: m_ref, l, l_exact
+  if (g4 == 0) {
+    stat[(w * 32 + c16) * 3 + 0] = m_x;
+    stat[(w * 32 + c16) * 3 + 1] = ltx;
+    stat[(w * 32 + c16) * 3 + 2] = lex;
+    stat[(w * 32 + 16 + c16) * 3 + 0] = m_y;
+    stat[(w * 32 + 16 + c16) * 3 + 1] = lty;
+    stat[(w * 32 + 16 + c16) * 3 + 2] = ley;
+  }
+  __syncthreads();
+  // the lane's P.V row lrow over the four streams (every wave forms the same values for all 32 rows)
+  float m = -INFINITY;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) m = fmaxf(m, stat[(s * 32 + lrow) * 3]);
+  float a_s[4], l = 0.f, lexact = 0.f;
+  bool redo_row = false;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const float* st = stat + (s * 32 + lrow) * 3;
+    a_s[s] = st[0] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(st[0] - m);
+    l += st[1] * a_s[s];
+    lexact += st[2] * a_s[s];
+    redo_row = redo_row || !(st[2] < kRowSumLimit);  // incl. +inf / NaN
+  }
+  const float inv = l > 0.f ? 1.0f / l : 0.f;
+  const float a_mine = w_uniform == 0 ? a_s[0] : w_uniform == 1 ? a_s[1] : w_uniform == 2 ? a_s[2] : a_s[3];
+  const float mine = a_mine * inv;
+  const bool row_valid = row0 + lrow < R;
+  const bool any_redo = __ballot(redo_row) != 0;
+  const uint64_t redo = __ballot(redo_row && hi == 0 && row_valid);
+  if (w_uniform == 0 && hi == 0 && row_valid)
+    p.lse_part[(int64_t)wi.bs * p.rows_pad + row0 + lrow] =
+        lexact > 0.f ? (m + __builtin_amdgcn_logf(lexact)) * kLn2 : -INFINITY;
+
+  // hand-over: giver w writes, for owner o != w, its 4 x 4 (block, quad) f16x4 of blocks 4o .. 4o + 3
+  // (8 x 16 B per lane) into dump (w, o); the stages follow the 12 dumps
+  constexpr int kDumpBytes4 = 8 * 64 * 16;
+  constexpr int kStageRowBytes4 = 256 + 16;  // one row's 128 fp16 columns + 16 B of padding
+  constexpr int kStageBytes4 = 32 * kStageRowBytes4;
+  static_assert(12 * kDumpBytes4 + kWaves * kStageBytes4 <= kRing * kTileBytes, "hand-over and staging fit the ring");
+  auto dump_at = [&](int giver, int owner) {
+    return smem + (giver * 3 + (owner < giver ? owner : owner - 1)) * kDumpBytes4;
+  };
+  auto weighted = [&](int b, int q4) {  // column block b, quad q4 of the lane: 4 weighted fp16 values
+    f16x4 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = (_Float16)(acc_read(o_acc[b][4 * q4 + e]) * mine);
+    return v;
+  };
+#pragma unroll
+  for (int o = 0; o < 4; ++o) {
+    if (o == w_uniform) continue;
+    lds_char* d = dump_at(w_uniform, o);
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {  // (block, quad) pairs 2jj, 2jj + 1 of the 16 handed to o
+      const int v0 = 2 * jj, v1 = 2 * jj + 1;
+      const f16x4 x0 = weighted(4 * o + (v0 >> 2), v0 & 3), x1 = weighted(4 * o + (v1 >> 2), v1 & 3);
+      *(__attribute__((address_space(3))) i32x4*)(d + (jj * 64 + lane) * 16) =
+          __builtin_shufflevector(__builtin_bit_cast(i32x2, x0), __builtin_bit_cast(i32x2, x1), 0, 1, 2, 3);
+    }
+  }
+  __syncthreads();  // every wave's hand-overs are in LDS
+  lds_char* stage = smem + 12 * kDumpBytes4 + w_uniform * kStageBytes4;
+  auto keep = [&](auto o_c) __attribute__((always_inline)) {
+    constexpr int o = decltype(o_c)::value;  // == w
+    i32x4 dd[3][8];  // the three givers' dumps, in giver order; all reads go out before any is used
+#pragma unroll
+    for (int gi = 0; gi < 3; ++gi) {
+      const int giver = gi < o ? gi : gi + 1;
+      const lds_char* d = dump_at(giver, o);
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) dd[gi][jj] = *(const __attribute__((address_space(3))) i32x4*)(d + (jj * 64 + lane) * 16);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int b = 4 * o + (v >> 2), q4 = v & 3;
+      f16x4 rr[3];
+#pragma unroll
+      for (int gi = 0; gi < 3; ++gi) {
+        const i32x4 d = dd[gi][v >> 1];
+        rr[gi] = __builtin_bit_cast(f16x4, (v & 1) ? (i32x2){d[2], d[3]} : (i32x2){d[0], d[1]});
+      }
+      f16x4 out;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        out[e] = (_Float16)(acc_read(o_acc[b][4 * q4 + e]) * mine + (float)rr[0][e] + (float)rr[1][e] + (float)rr[2][e]);
+      const int cb = (32 * (v >> 2) + 8 * q4 + 4 * hi) * 2;  // byte column within the wave's 128 columns
+      *(__attribute__((address_space(3))) f16x4*)(stage + lrow * kStageRowBytes4 + cb) = out;
+    }
+  };
+  if (w_uniform == 0) keep(std::integral_constant<int, 0>{});
+  else if (w_uniform == 1) keep(std::integral_constant<int, 1>{});
+  else if (w_uniform == 2) keep(std::integral_constant<int, 2>{});
+  else keep(std::integral_constant<int, 3>{});
+  {
+    // the wave's 32 staged rows, four rows per store instruction (16 lanes x 16 B per row); the wave
+    // reads back only what it staged itself, so no barrier is needed here
+    uint16_t* part_base = p.o_part + ((int64_t)wi.bs * p.rows_pad + row0) * kDv + w_uniform * (kDv / 4) + (lane & 15) * 8;
+    i32x4 sv[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      sv[k] = *(const __attribute__((address_space(3))) i32x4*)(stage + (4 * k + g4) * kStageRowBytes4 + (lane & 15) * 16);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int r = 4 * k + g4;
+      if (row0 + r < R) store16_through(part_base + (int64_t)r * kDv, sv[k]);
+    }
+  }
+  if (any_redo) {
+    __syncthreads();  // (the global writes of all four waves are ordered by the barrier's release/acquire)
+    if (w_uniform == 0 && redo != 0) redo_rows_exact(p, wi, row0, (uint32_t)redo, 0, 1, wi.bs);
+  }
+}
+
 // Eight consecutive partial values: loaded raw (so that a batch of loads is in flight at
 // once), widened to fp32 when used.
 template <typename PartT>
@@ -1643,7 +2024,9 @@ hipError_t launch_partial(const PartialArgs& a, hipStream_t stream) {
     return hipGetLastError();
   }
   const int64_t grid = (int64_t)a.batch * a.nsplit * a.row_groups;
-  if (a.streams == 2)
+  if (a.streams == 4)
+    hipLaunchKernelGGL(mla_verify_partial_4s, dim3((unsigned)grid), dim3(kWaves * 64), 0, stream, MLAV_LEAD_OF(a), a);
+  else if (a.streams == 2)
     hipLaunchKernelGGL(mla_verify_partial_2s, dim3((unsigned)grid), dim3(kWaves * 64), 0, stream, MLAV_LEAD_OF(a), a);
   else
     hipLaunchKernelGGL(mla_verify_partial<false>, dim3((unsigned)grid), dim3(kWaves * 64), 0, stream, MLAV_LEAD_OF(a), a);

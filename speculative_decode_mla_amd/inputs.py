@@ -68,7 +68,7 @@ WORKLOADS = {
     "ctx91k": Workload("ctx91k", 1, 64, 16, 91000, 1 << 21, 32, 4),
     "batch16": Workload("batch16", 16, 64, 16, None, 1 << 22, 32, 5),
     # q_len = 1 decode steps (one token per request, no drafts to verify)
-    "decode64k": Workload("decode64k", 1, 64, 1, 65536, 1 << 21, 256, 6),
+    "decode64k": Workload("decode64k", 1, 64, 1, 65536, 1 << 21, 128, 6),
     # ctx64k with one key per 2,048-key chunk (one split each at nsplit 32) scoring ~60 nats for one row
     "ctx64k_sink": Workload("ctx64k_sink", 1, 64, 16, 65536, 1 << 21, 32, 3, sink_nats=60.0),
     "decode_batch16": Workload("decode_batch16", 16, 64, 1, None, 1 << 22, 32, 7),

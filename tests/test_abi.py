@@ -100,7 +100,7 @@ def test_host_validation_before_any_hip_call(lib):
     assert lib.mla_verify_create(ctypes.byref(bad), ctypes.byref(h)) == _lib.MLA_ERR_INVALID_ARGUMENT
     bad = _lib.MlaVerifyConfig(16, 576, 512, 1, 4, 1, 4096, float("nan"))
     assert lib.mla_verify_create(ctypes.byref(bad), ctypes.byref(h)) == _lib.MLA_ERR_INVALID_ARGUMENT
-    bad = _lib.MlaVerifyConfig(16, 576, 512, 1, 4, 1, 4096, 0.07, 3)  # no kernel form 3
+    bad = _lib.MlaVerifyConfig(16, 576, 512, 1, 4, 1, 4096, 0.07, 4)  # no kernel form 4
     assert lib.mla_verify_create(ctypes.byref(bad), ctypes.byref(h)) == _lib.MLA_ERR_INVALID_ARGUMENT
     assert h.value is None
 

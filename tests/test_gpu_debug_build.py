@@ -53,7 +53,7 @@ def test_valid_call_sets_no_flag_and_matches_release(api):
     assert e.value.status == _lib().MLA_ERR_UNSUPPORTED
 
 
-@pytest.mark.parametrize("form", [1, 2])
+@pytest.mark.parametrize("form", [1, 2, 3])
 def test_slot_outside_the_pool_is_clamped_and_flagged(api, form):
     """Slots past the pool's end and negative slots read the pool's last and first rows instead
     (which hold finite rows here): the result equals the oracle over the clamped slot list."""

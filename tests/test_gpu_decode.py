@@ -1,5 +1,6 @@
 """GPU parity for q_len = 1 decode steps (and other requests of at most 64 rows), which run the
-two-stream form of kernel 1: against the fp64 oracle, max |out err| <= 1e-2, max |lse err| <= 1e-3.
+two-stream form of kernel 1 (or, at few splits, the four-stream form), and the same cases in the
+four-stream form: against the fp64 oracle, max |out err| <= 1e-2, max |lse err| <= 1e-3.
 All calls go through the C ABI."""
 import math
 
@@ -22,14 +23,15 @@ def api():
     return A
 
 
-def _run_check(api, x, nsplit, label, max_q=None):
+def _run_check(api, x, nsplit, label, max_q=None, form=0):
     d = DeviceInputs(x)
-    h = api.MlaVerify(x.heads, len(x.seq_lens), max_q or int(max(1, x.q_lens.max())), nsplit, x.num_slots, x.scale)
+    h = api.MlaVerify(x.heads, len(x.seq_lens), max_q or int(max(1, x.q_lens.max())), nsplit, x.num_slots, x.scale,
+                      form=form)
     out, lse = d.run(h, nsplit)
     torch.cuda.synchronize()
     ref_o, ref_l = oracle.verify_attention(x.q, x.pool(), x.slot_idx, x.seq_lens, x.q_lens, x.scale)
     eo, el = max_errors(out, lse, ref_o, ref_l)
-    print(f"{label} nsplit={nsplit}: max|out err|={eo:.3e} max|lse err|={el:.3e}", flush=True)
+    print(f"{label} form={form} nsplit={nsplit}: max|out err|={eo:.3e} max|lse err|={el:.3e}", flush=True)
     assert eo <= OUT_TOL and el <= LSE_TOL
     return out, lse
 
@@ -47,17 +49,24 @@ CASES = [
 ]
 
 
+# 0: the library's choice; 3: the four-stream form (in which the cases above hold one, two, three or
+# four streams with keys, and one-key requests)
+DECODE_FORMS = [0, 3]
+
+
+@pytest.mark.parametrize("form", DECODE_FORMS)
 @pytest.mark.parametrize("seed,lens,qlens,heads,nsplit", CASES)
-def test_decode_cases(api, seed, lens, qlens, heads, nsplit):
+def test_decode_cases(api, seed, lens, qlens, heads, nsplit, form):
     x = I.make_custom(np.random.default_rng(seed), lens, qlens, heads, int(sum(lens)) * 2 + 64)
-    _run_check(api, x, nsplit, f"decode case {seed}")
+    _run_check(api, x, nsplit, f"decode case {seed}", form=form)
 
 
-def test_decode_split_count_does_not_change_result(api):
+@pytest.mark.parametrize("form", DECODE_FORMS)
+def test_decode_split_count_does_not_change_result(api, form):
     x = I.make_custom(np.random.default_rng(58), [5000], [1], 64, 12000)
     outs = []
     for ns in (1, 3, 16, 64):
-        out, _ = _run_check(api, x, ns, "decode split-count", max_q=1)
+        out, _ = _run_check(api, x, ns, "decode split-count", max_q=1, form=form)
         outs.append(bf16_to_f64(out))
     assert max(np.max(np.abs(o - outs[0])) for o in outs) <= OUT_TOL
 
@@ -73,7 +82,8 @@ def test_decode_overflow_fallback_rows(api, factor, lo, hi):
     streams are merged before the write)."""
     x = I.make_custom(np.random.default_rng(59), [3000], [1], 64, 6000)
     # key 2920 sits in tile 91: local tile 91 of the one split (nsplit 1) and 29 of the third split
-    # (nsplit 3 -> splits start at tiles 0, 31, 62), odd in both, so the second stream takes it.
+    # (nsplit 3 -> splits start at tiles 0, 31, 62), odd in both, so the second stream takes it (in the
+    # four-stream form it is in half tile 182 of the one split and 58 of the third: the third stream).
     # It is head 7's query with the span of the other 63 heads' queries projected out, times
     # `factor`: far above the rest for head 7, ~0 for every other head, and its v (dims 0..511)
     # stays ~factor * N(0,1), so head 7 is the only row it moves.
@@ -86,8 +96,9 @@ def test_decode_overflow_fallback_rows(api, factor, lo, hi):
     sc = x.scale * (oracle.bf16_bits_to_f64(x.kv_rows[:3000]) @ qv) / math.log(2.0)
     margin = float(sc[2920] - np.max(np.delete(sc, 2920)))
     assert lo < margin < hi, margin
-    _run_check(api, x, 3, f"decode planted x{factor}")
-    _run_check(api, x, 1, f"decode planted x{factor}")
+    for form in DECODE_FORMS:
+        _run_check(api, x, 3, f"decode planted x{factor}", form=form)
+        _run_check(api, x, 1, f"decode planted x{factor}", form=form)
 
 
 @pytest.mark.parametrize("workload", ["decode64k", "decode_batch16"])

@@ -25,8 +25,8 @@ def api():
 
 
 # Kernel-1 layouts: 1 = 128-row workgroups (range plan for batches of 2..64), 2 = two-stream 64-row
-# workgroups.  Tests that pin one run it under both.
-FORMS = [1, 2]
+# workgroups, 3 = four-stream 32-row workgroups.  Tests that pin one run it under each.
+FORMS = [1, 2, 3]
 
 
 def _handle(api, x, nsplit, max_q=None, form=0):
@@ -120,6 +120,13 @@ def _random_batch_cases():
 def test_random_batches_whole_tensor(api, seed, lens, qlens, heads, nsplit, form):
     x = I.make_custom(np.random.default_rng(seed), lens, qlens, heads, 2 * int(sum(lens)) + 64)
     _check(api, x, nsplit, f"batch{seed} B={len(lens)} H={heads}", form)
+
+
+@pytest.mark.parametrize("seed,lens,qlens,heads,nsplit", [c[:5] for c in _random_batch_cases()])
+def test_random_batches_four_stream(api, seed, lens, qlens, heads, nsplit):
+    """The same random batches in the four-stream form."""
+    x = I.make_custom(np.random.default_rng(seed), lens, qlens, heads, 2 * int(sum(lens)) + 64)
+    _check(api, x, nsplit, f"batch{seed} B={len(lens)} H={heads}", 3)
 
 
 def test_ctx4k_workload(api):

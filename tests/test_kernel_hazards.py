@@ -12,7 +12,8 @@ from tests import asm_hazards
 KERNELS = os.path.join(build.HERE, "csrc", "mla_verify_kernels.hip")
 FUNCTIONS = ["_ZN4mlav18mla_verify_partialILb0EEEvPKiS2_iiiiiNS_11PartialArgsE",  # per-request splits
              "_ZN4mlav18mla_verify_partialILb1EEEvPKiS2_iiiiiNS_11PartialArgsE",  # range plan
-             "_ZN4mlav21mla_verify_partial_2sEPKiS1_iiiiiNS_11PartialArgsE"]
+             "_ZN4mlav21mla_verify_partial_2sEPKiS1_iiiiiNS_11PartialArgsE",
+             "_ZN4mlav21mla_verify_partial_4sEPKiS1_iiiiiNS_11PartialArgsE"]
 
 
 @pytest.fixture(scope="module")

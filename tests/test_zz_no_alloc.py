@@ -45,11 +45,13 @@ def _compare(api, x, nsplit, label):
 
 def test_noalloc_equals_handle_call_on_shrinking_calls(api):
     # 1,024 rows at nsplit 32 (32.1 MiB of partials, the 128-row form), then a smaller batch through
-    # the range plan, then a decode step at nsplit 256, then the first shape again
+    # the range plan, then a decode step at nsplit 256 (two-stream form) and at nsplit 16 (four-stream
+    # form), then the first shape again
     big = I.make_custom(np.random.default_rng(70), [9000], [16], 64, 20000)
     _compare(api, big, 32, "one request, 128-row form")
     _compare(api, I.make_custom(np.random.default_rng(71), [700, 300, 41], [8, 8, 3], 16, 3000), 4, "batch, range plan")
     _compare(api, I.make_custom(np.random.default_rng(72), [4000], [1], 64, 9000), 256, "decode step")
+    _compare(api, I.make_custom(np.random.default_rng(74), [3000], [1], 64, 7000), 16, "decode step, four streams")
     _compare(api, big, 32, "one request again")
 
 
