@@ -1413,10 +1413,13 @@ void mla_verify_partial_2s(MLAV_LEAD_ARGS, PartialArgs args) {
 // ---- Kernel 1, four-stream form: 32-row workgroups ---------------------------------------------------
 // For calls whose two-stream grid would still leave at least half of the CUs idle (a short context
 // with few splits, a q_len = 1 decode step with few splits): the four waves hold the same 32 rows and
-// run four key streams over the split, in 16-key half tiles, half tile j to wave j % 4.  Each wave
-// gathers, multiplies and accumulates its own half tiles in two half-tile buffers (keys 0..15 and
-// 16..31 of ring buffer w), so the step loop has no barrier.  At the end the four streams'
-// accumulators are combined through LDS, as in the two-stream form, into one partial per split.
+// run four key streams over the split, in 16-key half tiles, half tile j to wave j % 4.  Wave w
+// gathers its stream's half tiles into two half-tile buffers (keys 0..15 and 16..31 of ring buffer
+// w) and computes their Q.K and softmax; the probabilities of the four streams go through LDS, and
+// wave w accumulates P.V over every stream's keys for its own 128 output columns (column blocks
+// 4w .. 4w + 3).  So the streams share one softmax reference per row (the row max over the first
+// half tiles of all four, plus the headroom), a wave holds 64 accumulators, and the partial needs
+// no merge between the waves at the end.
 //   * Q.K on MFMA 16x16x32 bf16 as S^T = K . Q^T, one MFMA per 16-row half of the rows: the A
 //     operand (16 keys x 32 dims) comes from the half-tile buffer, the B operand (32 dims x 16 rows)
 //     is resident (36 fragments: 18 dim steps x 2 row halves).  In the C layout lane l holds keys
@@ -1425,9 +1428,18 @@ void mla_verify_partial_2s(MLAV_LEAD_ARGS, PartialArgs args) {
 //     permlane16 swap and a permlane32 swap of the bf16-packed probabilities give lane l eight keys of
 //     row l % 32 in the key order of the 32x32 S^T layout's first 16-key step, which the V^T
 //     fragments already follow: keys 0-3, 8-11 in lanes 0..31 and 4-7, 12-15 in lanes 32..63.
+//   * A step: wait for the own half tile; barrier (every stream's half tile k has landed, every wave
+//     is done with step k - 1's buffers and probabilities); Q.K with the gathers of the next half
+//     tile and the first V^T fragments between its MFMAs; softmax, P to LDS; barrier; P.V over the
+//     four streams' P, the row sums between its MFMAs.
 constexpr int kHalfTileBytes = 2 * kKeyBlockBytes;  // 16 keys
 constexpr int kQkSteps16 = kDqk / 32;               // 18 dim steps of MFMA 16x16x32
+constexpr int kOwnBlocks4s = kColBlocks / 4;        // output column blocks of a wave
+constexpr int kPvFrags4s = 4 * kOwnBlocks4s;        // V^T fragments of a wave per step (four streams)
 static_assert(kQkSteps16 == 2 * kDmaPerTile, "one gather load per Q.K dim step");
+// beside the ring: every stream's P of the step, the first half tiles' row maxima, the row statistics
+constexpr int kPBufOff4s = 0, kRowMaxOff4s = 4 * 1024, kStatOff4s = kRowMaxOff4s + 4 * 32 * 4;
+static_assert(kStatOff4s + (4 * 32 * 2 + 32) * 4 <= kXchgBytes, "exchange areas fit");
 
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void mla_verify_partial_4s(MLAV_LEAD_ARGS, PartialArgs args) {
@@ -1440,6 +1452,7 @@ void mla_verify_partial_4s(MLAV_LEAD_ARGS, PartialArgs args) {
   if (!decode_work(p, blockIdx.x, kRowsPerGroup4s, wi)) return;
   const int L = wi.L, Q = wi.Q, H = p.heads, R = wi.R;
   const int nh = 2 * (wi.t_end - wi.t_begin);  // 16-key half tiles of the split
+  const int nsteps = (nh + 3) / 4;             // (stream 0 has the most half tiles)
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int w_uniform = __builtin_amdgcn_readfirstlane(w);
@@ -1450,7 +1463,8 @@ void mla_verify_partial_4s(MLAV_LEAD_ARGS, PartialArgs args) {
   const int limx = L - Q + (rx < R ? rx / H : 0) + 1;  // row x sees keys [0, limx)
   const int limy = L - Q + (ry < R ? ry / H : 0) + 1;
   const int mask_from = L - Q + 1;  // first key some draft row cannot see
-  const int nst = nh > w_uniform ? (nh - w_uniform + 3) / 4 : 0;  // this stream's half tiles
+  auto nst_of = [&](int s) { return nh > s ? (nh - s + 3) / 4 : 0; };  // half tiles of stream s
+  const int nst = nst_of(w_uniform);
 
   // ---- gather set-up: the wave moves both key blocks (keys 0..7, 8..15) of its half tile k (the
   // split's half tile 4k + w) into half-buffer k & 1 of ring buffer w; keys past the request's end
@@ -1532,23 +1546,28 @@ void mla_verify_partial_4s(MLAV_LEAD_ARGS, PartialArgs args) {
       for (int r = 0; r < 2; ++r)
         vaddr[e][r] = r * kKeyBlockBytes + kr * 128 + (((4 * e) ^ u ^ kr ^ r) << 4) + (j & 1) * 8;
   }
-  // O^T of the group's 32 rows over this stream's keys, all 512 columns
-  f32x16 o_acc[kColBlocks];
+  // O^T of the group's 32 rows over all the split's keys, the wave's 128 columns
+  f32x16 o_acc[kOwnBlocks4s];
 #pragma unroll
-  for (int c = 0; c < kColBlocks; ++c) {
+  for (int c = 0; c < kOwnBlocks4s; ++c) {
     o_acc[c] = (f32x16){};
     asm volatile("" : "+a"(o_acc[c]));  // zeroed here, in AGPRs (see the two-stream form)
   }
-  // the stream's softmax state for rows x and y (the lane's share of the row sums)
+  // the reference of rows x and y (shared by the streams) and this stream's share of their row sums
   float m_x = -INFINITY, m_y = -INFINITY, nm_x = 0.f, nm_y = 0.f;
   float lr_x = 0.f, lr_y = 0.f, le_x = 0.f, le_y = 0.f;
+  lds_char* xchg = smem + kRing * kTileBytes;
+  float* rmax = (float*)(smem_raw + kRing * kTileBytes + kRowMaxOff4s);  // [stream][32 rows]: raw row max
   bf16x8 kf[kQkSteps16];
   auto kread = [&](const lds_char* hb, int ks) {
     kf[ks] = *(const __attribute__((address_space(3))) bf16x8*)(hb + kaddr16[ks & 1] + (ks >> 1) * kBlockBytes);
   };
-  bf16x8 vf[kColBlocks];  // V^T fragment of column block n over the half tile's 16 keys
-  auto vread = [&](const lds_char* hb, int n) {
-    const lds_char* vb = hb + (n >> 1) * kBlockBytes;
+  bf16x8 vf[kPvFrags4s];  // V^T fragment n: stream n / 4's half tile, column block 4w + n % 4
+  // (a stream without a half tile in the step reads stream 0's, and its P is zero)
+  auto vread = [&](int k, int n) {
+    const int s = k < nst_of(n >> 2) ? (n >> 2) : 0;
+    const lds_char* vb = smem + s * kTileBytes + (k & 1) * kHalfTileBytes +
+                         (2 * w_uniform + ((n & 3) >> 1)) * kBlockBytes;
     const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (__attribute__((address_space(3))) i16x4*)(vb + vaddr[n & 1][0]));
     const i16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -1556,93 +1575,125 @@ void mla_verify_partial_4s(MLAV_LEAD_ARGS, PartialArgs args) {
     vf[n] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
   };
 
-  for (int k = 0; k < nst; ++k) {
+  for (int k = 0; k < nsteps; ++k) {
+    const bool active = k < nst;
     const lds_char* hb = smem + w_uniform * kTileBytes + (k & 1) * kHalfTileBytes;
     MLAV_WAIT_VMCNT(0);  // this wave's half tile k (and the slot loads for the next gather) have landed
-    const bool refill = k + 1 < nst;
-    const char* r0 = g_row(checked_slot(sn[0], p.num_slots, p.debug_flags), 0);
-    const char* r1 = g_row(checked_slot(sn[1], p.num_slots, p.debug_flags), 1);
-    if (refill) {
-#pragma unroll
-      for (int j = 0; j < 2; ++j) sn[j] = slots_g[gather_key(k + 2, j)];
-    }
-    const uint32_t l0 = g_lds(k + 1, 0), l1 = g_lds(k + 1, 1);
-    // Q.K of half tile k for both row halves, the gathers of half tile k + 1 between the MFMAs, the
-    // first V^T fragments in the last dim steps
+    __syncthreads();     // every stream's half tile k is visible; every wave is done with step k - 1
     f32x4 sx, sy;
-#pragma unroll
-    for (int ks = 0; ks < kPrefetch; ++ks) kread(hb, ks);
-#pragma unroll
-    for (int ks = 0; ks < kQkSteps16; ++ks) {
-      __builtin_amdgcn_sched_barrier(0);
-      if (ks + kPrefetch < kQkSteps16) kread(hb, ks + kPrefetch);
-      if (ks >= kQkSteps16 - kVPrefetch) vread(hb, ks - (kQkSteps16 - kVPrefetch));
-      __builtin_amdgcn_sched_barrier(0);
-      if (ks == 0) {
-        mfma16_first_v(sx, kf[ks], qf[0][ks]);
-        mfma16_first_v(sy, kf[ks], qf[1][ks]);
-      } else {
-        mfma16_acc_v(sx, kf[ks], qf[0][ks]);
-        mfma16_acc_v(sy, kf[ks], qf[1][ks]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
+    if (active) {
+      const bool refill = k + 1 < nst;
+      const char* r0 = g_row(checked_slot(sn[0], p.num_slots, p.debug_flags), 0);
+      const char* r1 = g_row(checked_slot(sn[1], p.num_slots, p.debug_flags), 1);
       if (refill) {
-        if (ks < kDmaPerTile) dma_chunk_group(r0, l0, ks);
-        else dma_chunk_group(r1, l1, ks - kDmaPerTile);
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile(MLAV_MFMA_DRAIN : "+v"(sx), "+v"(sy));
-    const int key0 = (2 * wi.t_begin + 4 * k + w_uniform) * 16 + 4 * g4;  // the lane's first key
-    if (key0 - 4 * g4 + 16 > mask_from) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        sx[r] = key0 + r < limx ? sx[r] : -INFINITY;
-        sy[r] = key0 + r < limy ? sy[r] : -INFINITY;
+        for (int j = 0; j < 2; ++j) sn[j] = slots_g[gather_key(k + 2, j)];
       }
+      const uint32_t l0 = g_lds(k + 1, 0), l1 = g_lds(k + 1, 1);
+      // Q.K of half tile k for both row halves, the gathers of half tile k + 1 between the MFMAs, the
+      // first V^T fragments (stream 0's) in the last dim steps
+#pragma unroll
+      for (int ks = 0; ks < kPrefetch; ++ks) kread(hb, ks);
+#pragma unroll
+      for (int ks = 0; ks < kQkSteps16; ++ks) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (ks + kPrefetch < kQkSteps16) kread(hb, ks + kPrefetch);
+        if (ks >= kQkSteps16 - kVPrefetch) vread(k, ks - (kQkSteps16 - kVPrefetch));
+        __builtin_amdgcn_sched_barrier(0);
+        if (ks == 0) {
+          mfma16_first_v(sx, kf[ks], qf[0][ks]);
+          mfma16_first_v(sy, kf[ks], qf[1][ks]);
+        } else {
+          mfma16_acc_v(sx, kf[ks], qf[0][ks]);
+          mfma16_acc_v(sy, kf[ks], qf[1][ks]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (refill) {
+          if (ks < kDmaPerTile) dma_chunk_group(r0, l0, ks);
+          else dma_chunk_group(r1, l1, ks - kDmaPerTile);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile(MLAV_MFMA_DRAIN : "+v"(sx), "+v"(sy));
+      const int key0 = (2 * wi.t_begin + 4 * k + w_uniform) * 16 + 4 * g4;  // the lane's first key
+      if (key0 - 4 * g4 + 16 > mask_from) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          sx[r] = key0 + r < limx ? sx[r] : -INFINITY;
+          sy[r] = key0 + r < limy ? sy[r] : -INFINITY;
+        }
+      }
+    } else {
+      // (a stream without a half tile in the split's last step: stream 0's V^T fragments without
+      // prefetch, and a zero P for the others)
+#pragma unroll
+      for (int n = 0; n < kVPrefetch; ++n) vread(k, n);
+      *(__attribute__((address_space(3))) i32x4*)(xchg + kPBufOff4s + (w * 64 + lane) * 16) = (i32x4){0, 0, 0, 0};
     }
-    if (k == 0) {  // the stream's references: the row maxima of its first half tile (see the 128-row form)
-      m_x = quad_max(fmaxf(fmaxf(sx[0], sx[1]), fmaxf(sx[2], sx[3]))) * p.scale_log2 + kRefHeadroom;
-      m_y = quad_max(fmaxf(fmaxf(sy[0], sy[1]), fmaxf(sy[2], sy[3]))) * p.scale_log2 + kRefHeadroom;
+    if (k == 0) {  // the shared references: the row maxima of the four streams' first half tiles
+      const float mx = active ? quad_max(fmaxf(fmaxf(sx[0], sx[1]), fmaxf(sx[2], sx[3]))) : -INFINITY;
+      const float my = active ? quad_max(fmaxf(fmaxf(sy[0], sy[1]), fmaxf(sy[2], sy[3]))) : -INFINITY;
+      if (g4 == 0) {
+        rmax[w * 32 + c16] = mx;
+        rmax[w * 32 + 16 + c16] = my;
+      }
+      __syncthreads();
+      float ax = rmax[c16], ay = rmax[16 + c16];
+#pragma unroll
+      for (int s = 1; s < 4; ++s) {
+        ax = fmaxf(ax, rmax[s * 32 + c16]);
+        ay = fmaxf(ay, rmax[s * 32 + 16 + c16]);
+      }
+      m_x = ax * p.scale_log2 + kRefHeadroom;
+      m_y = ay * p.scale_log2 + kRefHeadroom;
       nm_x = (m_x == -INFINITY) ? 0.f : -m_x;
       nm_y = (m_y == -INFINITY) ? 0.f : -m_y;
     }
-    float ex[4], ey[4];
+    if (active) {
+      float ex[4], ey[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) ex[r] = vfma(sx[r], p.scale_log2, nm_x);
+      for (int r = 0; r < 4; ++r) ex[r] = vfma(sx[r], p.scale_log2, nm_x);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) ey[r] = vfma(sy[r], p.scale_log2, nm_y);
+      for (int r = 0; r < 4; ++r) ey[r] = vfma(sy[r], p.scale_log2, nm_y);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) ex[r] = vexp2(ex[r]);
+      for (int r = 0; r < 4; ++r) ex[r] = vexp2(ex[r]);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) ey[r] = vexp2(ey[r]);
-    const int px0 = vpack_bf16(ex[0], ex[1]), px1 = vpack_bf16(ex[2], ex[3]);
-    const int py0 = vpack_bf16(ey[0], ey[1]), py1 = vpack_bf16(ey[2], ey[3]);
-    // lanes of rows 0..15 give their row 16.. keys to, and take their own row's next keys from, the
-    // lanes 16 above (permlane16), then the halves swap (permlane32): see the layout note above
-    const auto s0 = __builtin_amdgcn_permlane16_swap(px0, py0, false, false);
-    const auto s1 = __builtin_amdgcn_permlane16_swap(px1, py1, false, false);
-    const auto t0 = __builtin_amdgcn_permlane32_swap(s0[0], s0[1], false, false);
-    const auto t1 = __builtin_amdgcn_permlane32_swap(s1[0], s1[1], false, false);
-    i32x4 pv = (i32x4){(int)t0[0], (int)t1[0], (int)t0[1], (int)t1[1]};
-    // wait states between the swaps and the first MFMA reading their results (the operand ties the
-    // nop to the swaps, which the compiler would otherwise schedule past it)
-    asm volatile("s_nop 3" : "+v"(pv));
-    const bf16x8 pb = __builtin_bit_cast(bf16x8, pv);
-    // P.V over the 16 column blocks; the row sums between the MFMAs
+      for (int r = 0; r < 4; ++r) ey[r] = vexp2(ey[r]);
+      const int px0 = vpack_bf16(ex[0], ex[1]), px1 = vpack_bf16(ex[2], ex[3]);
+      const int py0 = vpack_bf16(ey[0], ey[1]), py1 = vpack_bf16(ey[2], ey[3]);
+      // lanes of rows 0..15 give their row 16.. keys to, and take their own row's next keys from, the
+      // lanes 16 above (permlane16), then the halves swap (permlane32): see the layout note above
+      const auto s0 = __builtin_amdgcn_permlane16_swap(px0, py0, false, false);
+      const auto s1 = __builtin_amdgcn_permlane16_swap(px1, py1, false, false);
+      const auto t0 = __builtin_amdgcn_permlane32_swap(s0[0], s0[1], false, false);
+      const auto t1 = __builtin_amdgcn_permlane32_swap(s1[0], s1[1], false, false);
+      *(__attribute__((address_space(3))) i32x4*)(xchg + kPBufOff4s + (w * 64 + lane) * 16) =
+          (i32x4){(int)t0[0], (int)t1[0], (int)t0[1], (int)t1[1]};
+      // the stream's row sums (while the other streams reach the barrier)
 #pragma unroll
-    for (int n = 0; n < kColBlocks; ++n) {
+      for (int r = 0; r < 4; ++r) vadd_to(le_x, ex[r]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) vadd_to(le_y, ey[r]);
+      vsum_pair_to(lr_x, px0);
+      vsum_pair_to(lr_x, px1);
+      vsum_pair_to(lr_y, py0);
+      vsum_pair_to(lr_y, py1);
+    }
+    __syncthreads();  // every active stream's P of the step is in LDS
+    // P.V: the four streams' P (those with a half tile in this step) times their V^T fragments for the
+    // wave's column blocks; stream s's P is read two MFMAs before its first one
+    auto pread = [&](int s) {
+      return *(const __attribute__((address_space(3))) bf16x8*)(xchg + kPBufOff4s + (s * 64 + lane) * 16);
+    };
+    bf16x8 pb[4];
+    pb[0] = pread(0);
+#pragma unroll
+    for (int n = 0; n < kPvFrags4s; ++n) {
       __builtin_amdgcn_sched_barrier(0);
-      if (n + kVPrefetch < kColBlocks) vread(hb, n + kVPrefetch);
+      if (n + kVPrefetch < kPvFrags4s) vread(k, n + kVPrefetch);
+      if ((n & 3) == 2 && n + 2 < kPvFrags4s) pb[(n + 2) >> 2] = pread((n + 2) >> 2);
       __builtin_amdgcn_sched_barrier(0);
-      mfma_acc_a(o_acc[n], vf[n], pb);
-      __builtin_amdgcn_sched_barrier(0);
-      if (n < 4) vadd_to(le_x, ex[n]);
-      else if (n < 8) vadd_to(le_y, ey[n - 4]);
-      else if (n == 8) vsum_pair_to(lr_x, px0);
-      else if (n == 9) vsum_pair_to(lr_x, px1);
-      else if (n == 10) vsum_pair_to(lr_y, py0);
-      else if (n == 11) vsum_pair_to(lr_y, py1);
+      mfma_acc_a(o_acc[n & 3], vf[n], pb[n >> 2]);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -1650,41 +1701,32 @@ void mla_verify_partial_4s(MLAV_LEAD_ARGS, PartialArgs args) {
   // The accumulators are read below only through acc_read (volatile), which stays behind this drain.
   asm volatile(MLAV_MFMA_DRAIN);
 
-  // ---- merge of the four streams, then the partial write.  With m = max_s m_s, a_s = 2^(m_s - m):
-  // l = sum_s a_s l_s and O = sum_s a_s O_s.  The per-row (m_s, l_s, l_exact_s) go through LDS; wave w
-  // writes column blocks 4w .. 4w + 3 and first hands every other wave its weighted contribution to
-  // that wave's blocks, rounded to fp16 (as in the two-stream form).  A row where any stream's sum
-  // outgrew its reference is redone exactly over the whole split.
+  // ---- the partial: the row sums of the four streams (one reference, so plain sums) through LDS,
+  // then each wave normalises, stages and stores its 32 rows x 128 columns.  A row whose sum outgrew
+  // the reference is redone exactly over the whole split.
   const float ltx = quad_sum(lr_x), lty = quad_sum(lr_y);
   const float lex = quad_sum(le_x), ley = quad_sum(le_y);
-  __syncthreads();  // every wave is done with the ring
-  float* stat = (float*)(smem_raw + kRing * kTileBytes);  // [wave][32 rows][3]: m_ref, l, l_exact
+  float* stat = (float*)(smem_raw + kRing * kTileBytes + kStatOff4s);  // [stream][32 rows][2]: l, l_exact; then m[32]
   if (g4 == 0) {
-    stat[(w * 32 + c16) * 3 + 0] = m_x;
-    stat[(w * 32 + c16) * 3 + 1] = ltx;
-    stat[(w * 32 + c16) * 3 + 2] = lex;
-    stat[(w * 32 + 16 + c16) * 3 + 0] = m_y;
-    stat[(w * 32 + 16 + c16) * 3 + 1] = lty;
-    stat[(w * 32 + 16 + c16) * 3 + 2] = ley;
+    stat[(w * 32 + c16) * 2 + 0] = ltx;
+    stat[(w * 32 + c16) * 2 + 1] = lex;
+    stat[(w * 32 + 16 + c16) * 2 + 0] = lty;
+    stat[(w * 32 + 16 + c16) * 2 + 1] = ley;
+    if (w == 0) {
+      stat[4 * 32 * 2 + c16] = m_x;
+      stat[4 * 32 * 2 + 16 + c16] = m_y;
+    }
   }
-  __syncthreads();
-  // the lane's P.V row lrow over the four streams (every wave forms the same values for all 32 rows)
-  float m = -INFINITY;
-#pragma unroll
-  for (int s = 0; s < 4; ++s) m = fmaxf(m, stat[(s * 32 + lrow) * 3]);
-  float a_s[4], l = 0.f, lexact = 0.f;
-  bool redo_row = false;
+  __syncthreads();  // (also: every wave is done with the ring)
+  float l = 0.f, lexact = 0.f;
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
-    const float* st = stat + (s * 32 + lrow) * 3;
-    a_s[s] = st[0] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(st[0] - m);
-    l += st[1] * a_s[s];
-    lexact += st[2] * a_s[s];
-    redo_row = redo_row || !(st[2] < kRowSumLimit);  // incl. +inf / NaN
+    l += stat[(s * 32 + lrow) * 2 + 0];
+    lexact += stat[(s * 32 + lrow) * 2 + 1];
   }
+  const float m = stat[4 * 32 * 2 + lrow];
   const float inv = l > 0.f ? 1.0f / l : 0.f;
-  const float a_mine = w_uniform == 0 ? a_s[0] : w_uniform == 1 ? a_s[1] : w_uniform == 2 ? a_s[2] : a_s[3];
-  const float mine = a_mine * inv;
+  const bool redo_row = !(lexact < kRowSumLimit);  // incl. +inf / NaN
   const bool row_valid = row0 + lrow < R;
   const bool any_redo = __ballot(redo_row) != 0;
   const uint64_t redo = __ballot(redo_row && hi == 0 && row_valid);
@@ -1692,67 +1734,18 @@ void mla_verify_partial_4s(MLAV_LEAD_ARGS, PartialArgs args) {
     p.lse_part[(int64_t)wi.bs * p.rows_pad + row0 + lrow] =
         lexact > 0.f ? (m + __builtin_amdgcn_logf(lexact)) * kLn2 : -INFINITY;
 
-  // hand-over: giver w writes, for owner o != w, its 4 x 4 (block, quad) f16x4 of blocks 4o .. 4o + 3
-  // (8 x 16 B per lane) into dump (w, o); the stages follow the 12 dumps
-  constexpr int kDumpBytes4 = 8 * 64 * 16;
   constexpr int kStageRowBytes4 = 256 + 16;  // one row's 128 fp16 columns + 16 B of padding
   constexpr int kStageBytes4 = 32 * kStageRowBytes4;
-  static_assert(12 * kDumpBytes4 + kWaves * kStageBytes4 <= kRing * kTileBytes, "hand-over and staging fit the ring");
-  auto dump_at = [&](int giver, int owner) {
-    return smem + (giver * 3 + (owner < giver ? owner : owner - 1)) * kDumpBytes4;
-  };
-  auto weighted = [&](int b, int q4) {  // column block b, quad q4 of the lane: 4 weighted fp16 values
-    f16x4 v;
+  static_assert(kWaves * kStageBytes4 <= kRing * kTileBytes, "staging fits the ring");
+  lds_char* stage = smem + w_uniform * kStageBytes4;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = (_Float16)(acc_read(o_acc[b][4 * q4 + e]) * mine);
-    return v;
-  };
+  for (int v = 0; v < 4 * kOwnBlocks4s; ++v) {  // (block, quad) v: columns 32 (v / 4) + 8 (v % 4) + 4 hi ..
+    const int b = v >> 2, q4 = v & 3;
+    f16x4 o;
 #pragma unroll
-  for (int o = 0; o < 4; ++o) {
-    if (o == w_uniform) continue;
-    lds_char* d = dump_at(w_uniform, o);
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {  // (block, quad) pairs 2jj, 2jj + 1 of the 16 handed to o
-      const int v0 = 2 * jj, v1 = 2 * jj + 1;
-      const f16x4 x0 = weighted(4 * o + (v0 >> 2), v0 & 3), x1 = weighted(4 * o + (v1 >> 2), v1 & 3);
-      *(__attribute__((address_space(3))) i32x4*)(d + (jj * 64 + lane) * 16) =
-          __builtin_shufflevector(__builtin_bit_cast(i32x2, x0), __builtin_bit_cast(i32x2, x1), 0, 1, 2, 3);
-    }
+    for (int e = 0; e < 4; ++e) o[e] = (_Float16)(acc_read(o_acc[b][4 * q4 + e]) * inv);
+    *(__attribute__((address_space(3))) f16x4*)(stage + lrow * kStageRowBytes4 + (32 * b + 8 * q4 + 4 * hi) * 2) = o;
   }
-  __syncthreads();  // every wave's hand-overs are in LDS
-  lds_char* stage = smem + 12 * kDumpBytes4 + w_uniform * kStageBytes4;
-  auto keep = [&](auto o_c) __attribute__((always_inline)) {
-    constexpr int o = decltype(o_c)::value;  // == w
-    i32x4 dd[3][8];  // the three givers' dumps, in giver order; all reads go out before any is used
-#pragma unroll
-    for (int gi = 0; gi < 3; ++gi) {
-      const int giver = gi < o ? gi : gi + 1;
-      const lds_char* d = dump_at(giver, o);
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) dd[gi][jj] = *(const __attribute__((address_space(3))) i32x4*)(d + (jj * 64 + lane) * 16);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int b = 4 * o + (v >> 2), q4 = v & 3;
-      f16x4 rr[3];
-#pragma unroll
-      for (int gi = 0; gi < 3; ++gi) {
-        const i32x4 d = dd[gi][v >> 1];
-        rr[gi] = __builtin_bit_cast(f16x4, (v & 1) ? (i32x2){d[2], d[3]} : (i32x2){d[0], d[1]});
-      }
-      f16x4 out;
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        out[e] = (_Float16)(acc_read(o_acc[b][4 * q4 + e]) * mine + (float)rr[0][e] + (float)rr[1][e] + (float)rr[2][e]);
-      const int cb = (32 * (v >> 2) + 8 * q4 + 4 * hi) * 2;  // byte column within the wave's 128 columns
-      *(__attribute__((address_space(3))) f16x4*)(stage + lrow * kStageRowBytes4 + cb) = out;
-    }
-  };
-  if (w_uniform == 0) keep(std::integral_constant<int, 0>{});
-  else if (w_uniform == 1) keep(std::integral_constant<int, 1>{});
-  else if (w_uniform == 2) keep(std::integral_constant<int, 2>{});
-  else keep(std::integral_constant<int, 3>{});
   {
     // the wave's 32 staged rows, four rows per store instruction (16 lanes x 16 B per row); the wave
     // reads back only what it staged itself, so no barrier is needed here
