@@ -18,7 +18,7 @@ constexpr int kRowsPerGroup2s = 2 * kRowsPerWave;  // rows per workgroup in the 
 constexpr int kRowsPerGroup4s = kRowsPerWave;      // rows per workgroup in the four-stream form: 32
 constexpr int kRangeMaxBatch = 64;   // the range plan holds one request per lane of a wave
 
-// Kernel 1: one workgroup per (request, split, 128-row group).
+// Kernel 1: one workgroup per (request, split, row group of 128, 64 or 32 rows by form).
 struct PartialArgs {
   const uint16_t* q;         // bf16 [T_q*H, 576]
   const uint16_t* kv;        // bf16 [num_slots, 576]

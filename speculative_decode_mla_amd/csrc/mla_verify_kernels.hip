@@ -3,8 +3,11 @@
 // Kernel 1 (mla_verify_partial) computes, for one request, one chunk ("split")
 // of its keys and 128 of its (draft token, head) rows, the softmax-attention
 // partial of those rows over those keys: o_s (normalised within the chunk) and
-// its natural-log LSE.  Kernel 2 (mla_verify_merge) reduces the partials of a
-// row into the bf16 output and the fp32 LSE.  This is the partial + reduce
+// its natural-log LSE.  Two more layouts of it serve calls with few rows or few
+// splits: mla_verify_partial_2s (64 rows, two key streams) and
+// mla_verify_partial_4s (32 rows, four key streams), further below.  Kernel 2
+// (mla_verify_merge) reduces the partials of a row into the bf16 output and the
+// fp32 LSE.  This is the partial + reduce
 // ("KV-split flash-decode") scheme of magik.net "The Decisive A/B", sections
 // "The Context" and "What This Reveals About the Bottleneck", laid out for
 // CDNA4 rather than for the sm_120 part the page targets.

@@ -61,7 +61,7 @@ CASES = [
     (26, [300], [16], 64, 2),           # 1024 rows: eight row groups
     (27, [4096 + 37], [16], 16, 8),     # ragged last tile
     (28, [64, 128, 192], [16, 16, 16], 4, 32),  # more splits than tiles
-    (29, [900], [5], 40, 4),            # 200 rows: a ragged last row group in either form
+    (29, [900], [5], 40, 4),            # 200 rows: a ragged last row group in every form
     (41, [2000], [16], 128, 8),         # 128 heads: 2,048 rows, 16 (or 32) row groups
     (42, [900, 1300], [16, 8], 128, 4),  # 128 heads in the range plan: 16 workers of 16 row groups
     (46, [16], [16], 64, 2),            # every key is a draft key: draft t sees keys 0..t only
@@ -364,7 +364,11 @@ def test_merge_kernel_alone(api, S):
     (64, [2500, 90, 1], [9, 3, 1], 24, 6, 1),    # ragged, forced 128-row form
     (65, [2500, 90, 1], [9, 3, 1], 24, 6, 2),    # ragged, forced two-stream form
     (66, [3000], [4], 8, 64, 0),                 # more splits asked for than the request fills
-], ids=["128-row", "two-stream", "range plan", "decode", "ragged 128-row", "ragged two-stream", "unused splits"])
+    (67, [4096], [8], 64, 8, 0),                 # one request, 8 x 16 row groups: four-stream form (automatic)
+    (68, [4000], [1], 64, 16, 0),                # a decode step at few splits: four-stream form (automatic)
+    (69, [2500, 90, 1], [9, 3, 1], 24, 6, 3),    # ragged, forced four-stream form (streams without keys)
+], ids=["128-row", "two-stream", "range plan", "decode", "ragged 128-row", "ragged two-stream", "unused splits",
+        "four-stream", "decode four-stream", "ragged four-stream"])
 def test_nan_workspace_is_not_read(api, seed, lens, qlens, heads, nsplit, form):
     """The split workspace filled with NaN before the call: every partial the merge reads must have
     been written by the same call, so out and lse come out finite and match the oracle."""
@@ -400,7 +404,8 @@ def test_stale_workspace_is_not_read(api):
     (43, [5000], [16], 64, 16),            # one request, 16 x 8 row groups: the two-stream form (automatic)
     (44, [9000], [16], 64, 32),            # one request, 32 x 8 row groups: the 128-row form
     (45, [4000, 700], [1, 1], 64, 32),     # a decode step: 64 rows per request, the two-stream form
-], ids=["range plan", "two-stream", "128-row", "decode"])
+    (46, [4096], [8], 64, 8),              # one request, 8 x 16 row groups: the four-stream form (automatic)
+], ids=["range plan", "two-stream", "128-row", "decode", "four-stream"])
 def test_graph_replay_matches_eager(api, seed, lens, qlens, heads, nsplit):
     x = I.make_custom(np.random.default_rng(seed), lens, qlens, heads, int(sum(lens)) * 2 + 64)
     d = DeviceInputs(x)
