@@ -1594,28 +1594,34 @@ void mla_verify_partial_4s(MLAV_LEAD_ARGS, PartialArgs args) {
       }
       const uint32_t l0 = g_lds(k + 1, 0), l1 = g_lds(k + 1, 1);
       // Q.K of half tile k for both row halves, the gathers of half tile k + 1 between the MFMAs, the
-      // first V^T fragments (stream 0's) in the last dim steps
+      // first V^T fragments (stream 0's) in the last dim steps.  (Two copies of the loop, with and
+      // without the gathers, so that no branch sits between its MFMAs.)
+      auto qk = [&](auto gather_c) __attribute__((always_inline)) {
+        constexpr bool kGather = decltype(gather_c)::value;
 #pragma unroll
-      for (int ks = 0; ks < kPrefetch; ++ks) kread(hb, ks);
+        for (int ks = 0; ks < kPrefetch; ++ks) kread(hb, ks);
 #pragma unroll
-      for (int ks = 0; ks < kQkSteps16; ++ks) {
-        __builtin_amdgcn_sched_barrier(0);
-        if (ks + kPrefetch < kQkSteps16) kread(hb, ks + kPrefetch);
-        if (ks >= kQkSteps16 - kVPrefetch) vread(k, ks - (kQkSteps16 - kVPrefetch));
-        __builtin_amdgcn_sched_barrier(0);
-        if (ks == 0) {
-          mfma16_first_v(sx, kf[ks], qf[0][ks]);
-          mfma16_first_v(sy, kf[ks], qf[1][ks]);
-        } else {
-          mfma16_acc_v(sx, kf[ks], qf[0][ks]);
-          mfma16_acc_v(sy, kf[ks], qf[1][ks]);
+        for (int ks = 0; ks < kQkSteps16; ++ks) {
+          __builtin_amdgcn_sched_barrier(0);
+          if (ks + kPrefetch < kQkSteps16) kread(hb, ks + kPrefetch);
+          if (ks >= kQkSteps16 - kVPrefetch) vread(k, ks - (kQkSteps16 - kVPrefetch));
+          __builtin_amdgcn_sched_barrier(0);
+          if (ks == 0) {
+            mfma16_first_v(sx, kf[ks], qf[0][ks]);
+            mfma16_first_v(sy, kf[ks], qf[1][ks]);
+          } else {
+            mfma16_acc_v(sx, kf[ks], qf[0][ks]);
+            mfma16_acc_v(sy, kf[ks], qf[1][ks]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          if constexpr (kGather) {
+            if (ks < kDmaPerTile) dma_chunk_group(r0, l0, ks);
+            else dma_chunk_group(r1, l1, ks - kDmaPerTile);
+          }
         }
-        __builtin_amdgcn_sched_barrier(0);
-        if (refill) {
-          if (ks < kDmaPerTile) dma_chunk_group(r0, l0, ks);
-          else dma_chunk_group(r1, l1, ks - kDmaPerTile);
-        }
-      }
+      };
+      if (refill) qk(std::true_type{});
+      else qk(std::false_type{});
       __builtin_amdgcn_sched_barrier(0);
       asm volatile(MLAV_MFMA_DRAIN : "+v"(sx), "+v"(sy));
       const int key0 = (2 * wi.t_begin + 4 * k + w_uniform) * 16 + 4 * g4;  // the lane's first key
