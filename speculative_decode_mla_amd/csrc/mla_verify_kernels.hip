@@ -1229,26 +1229,34 @@ void mla_verify_partial_2s(MLAV_LEAD_ARGS, PartialArgs args) {
     const uint32_t l0 = g_lds(k + 1, 0), l1 = g_lds(k + 1, 1);
     if (active) {
       SoftmaxTile sm;
-      // Q.K of tile k, the gathers of the stream's tile k+1 between its MFMAs
+      // Q.K of tile k, the gathers of the stream's tile k+1 between its MFMAs (two copies of the loop,
+      // with and without the gathers, so that no branch sits between its MFMAs)
       f32x16 sacc;
+      auto qk = [&](auto gather_c) __attribute__((always_inline)) {
+        constexpr bool kGather = decltype(gather_c)::value;
 #pragma unroll
-      for (int ks = 0; ks < kPrefetch; ++ks) kread(tb, ks);
+        for (int ks = 0; ks < kPrefetch; ++ks) kread(tb, ks);
 #pragma unroll
-      for (int ks = 0; ks < kQkSteps; ++ks) {
-        __builtin_amdgcn_sched_barrier(0);
-        if (ks + kPrefetch < kQkSteps) kread(tb, ks + kPrefetch);
-        // the first V^T fragments of the tile, for the P.V after the softmax
-        if (ks >= kQkSteps - kVPrefetch) vread(tb, ks - (kQkSteps - kVPrefetch));
-        __builtin_amdgcn_sched_barrier(0);
-        if (ks == 0) mfma_first_v(sacc, kf[ks], qf[ks]);
-        else mfma_acc_v(sacc, kf[ks], qf[ks]);
-        __builtin_amdgcn_sched_barrier(0);
-        if (refill && !(ks & 1) && (ks >> 1) < 2 * kDmaPerTile) {
-          const int j = ks >> 1;
-          if (j < kDmaPerTile) dma_chunk_group(r0, l0, j);
-          else dma_chunk_group(r1, l1, j - kDmaPerTile);
+        for (int ks = 0; ks < kQkSteps; ++ks) {
+          __builtin_amdgcn_sched_barrier(0);
+          if (ks + kPrefetch < kQkSteps) kread(tb, ks + kPrefetch);
+          // the first V^T fragments of the tile, for the P.V after the softmax
+          if (ks >= kQkSteps - kVPrefetch) vread(tb, ks - (kQkSteps - kVPrefetch));
+          __builtin_amdgcn_sched_barrier(0);
+          if (ks == 0) mfma_first_v(sacc, kf[ks], qf[ks]);
+          else mfma_acc_v(sacc, kf[ks], qf[ks]);
+          __builtin_amdgcn_sched_barrier(0);
+          if constexpr (kGather) {
+            if (!(ks & 1) && (ks >> 1) < 2 * kDmaPerTile) {
+              const int j = ks >> 1;
+              if (j < kDmaPerTile) dma_chunk_group(r0, l0, j);
+              else dma_chunk_group(r1, l1, j - kDmaPerTile);
+            }
+          }
         }
-      }
+      };
+      if (refill) qk(std::true_type{});
+      else qk(std::false_type{});
       __builtin_amdgcn_sched_barrier(0);
       asm volatile(MLAV_MFMA_DRAIN : "+v"(sacc));
       const int t = wi.t_begin + 2 * k + stream;
