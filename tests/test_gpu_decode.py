@@ -49,9 +49,10 @@ CASES = [
 ]
 
 
-# 0: the library's choice; 3: the four-stream form (in which the cases above hold one, two, three or
-# four streams with keys, and one-key requests)
-DECODE_FORMS = [0, 3]
+# 0: the library's choice (the four-stream form for most of these few-split cases, the two-stream form
+# past it); 2: the two-stream form; 3: the four-stream form (in which the cases above hold one, two,
+# three or four streams with keys, and one-key requests)
+DECODE_FORMS = [0, 2, 3]
 
 
 @pytest.mark.parametrize("form", DECODE_FORMS)
