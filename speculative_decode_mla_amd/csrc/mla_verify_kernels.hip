@@ -1089,7 +1089,7 @@ void mla_verify_partial_2s(MLAV_LEAD_ARGS, PartialArgs args) {
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int hi = lane >> 5, lrow = lane & 31;
-  const int stream = w >> 1;
+  const int stream = __builtin_amdgcn_readfirstlane(w) >> 1;  // (wave-uniform: the step's branches are scalar)
   const int half = w & 1;
   const int row0 = wi.g * kRowsPerGroup2s;
   const int myrow = row0 + half * kRowsPerWave + lrow;
