@@ -2,6 +2,7 @@
 states for them; check the generated gfx950 code for the MFMA hazards instead.
 CPU-only: it compiles the kernels to assembly, it runs nothing."""
 import os
+import re
 import shutil
 
 import pytest
@@ -33,6 +34,15 @@ def test_no_mfma_hazards(asm, fn):
     assert sum(asm_hazards.is_mfma(x) for x in insns) >= 68  # the whole main loop was parsed
     problems = asm_hazards.check(insns, labels)
     assert not problems, "\n".join(problems[:20])
+
+
+@pytest.mark.parametrize("fn", FUNCTIONS)
+def test_no_scratch(asm, fn):
+    """No kernel-1 form spills to scratch (a spill, or a register array the compiler could not keep in
+    registers, would be private memory traffic inside the step loop)."""
+    seg = asm[asm.index(fn + ":"):]
+    m = re.search(r"; ScratchSize: (\d+)", seg)
+    assert m is not None and int(m.group(1)) == 0, m.group(0) if m else "no ScratchSize line"
 
 
 @pytest.mark.parametrize("fn", FUNCTIONS)
