@@ -1441,8 +1441,8 @@ void mla_verify_partial_2s(MLAV_LEAD_ARGS, PartialArgs args) {
 //     fragments already follow: keys 0-3, 8-11 in lanes 0..31 and 4-7, 12-15 in lanes 32..63.
 //   * A step: wait for the own half tile; barrier (every stream's half tile k has landed, every wave
 //     is done with step k - 1's buffers and probabilities); Q.K with the gathers of the next half
-//     tile and the first V^T fragments between its MFMAs; softmax, P to LDS; barrier; P.V over the
-//     four streams' P, the row sums between its MFMAs.
+//     tile and the first V^T fragments between its MFMAs (two copies of that loop, with and without
+//     the gathers); softmax, P to LDS, the stream's row sums; barrier; P.V over the four streams' P.
 constexpr int kHalfTileBytes = 2 * kKeyBlockBytes;  // 16 keys
 constexpr int kQkSteps16 = kDqk / 32;               // 18 dim steps of MFMA 16x16x32
 constexpr int kOwnBlocks4s = kColBlocks / 4;        // output column blocks of a wave
