@@ -265,6 +265,12 @@ __device__ __forceinline__ void dma16(const void* gsrc, uint32_t m0_value) {
 __device__ __forceinline__ void store16_through(void* dst, const i32x4& v) {
   asm volatile("global_store_dwordx4 %0, %1, off sc1" : : "v"(dst), "v"(v) : "memory");
 }
+// ... at dst + OFF bytes (the instruction's immediate offset)
+template <int OFF>
+__device__ __forceinline__ void store16_through_at(void* dst, const i32x4& v) {
+  static_assert(OFF >= 0 && OFF < 4096, "immediate offset range");
+  asm volatile("global_store_dwordx4 %0, %1, off offset:%2 sc1" : : "v"(dst), "v"(v), "i"(OFF) : "memory");
+}
 
 // One wave's share of a tile: key block w (8 keys x 1152 B) as nine 1 KiB loads;
 // load cg moves 16-B chunks [8cg, 8cg+8) of the eight rows (see the layout above).
@@ -978,19 +984,33 @@ __device__ __forceinline__ void partial_item(const PartialArgs& p, const WorkIte
   // `between(k)` runs after the k-th store: the stores of the own rows go out between the
   // conversions of the partner's rows (the CU's store path and the VALU then work at once;
   // one after the other, the conversion and the store issue each took about 1 us).
+  // (a row group with all 128 rows valid, as in every group of a request with a multiple of 128 rows,
+  // stores without a per-row check, from one base address per two rows)
+  const bool full_group = row0 + kRowsPerGroup <= R;
   auto store_half = [&](const int r0, const int grow0, auto between) {  // stage rows r0 .. r0+31 = rows grow0 ..
     i32x4 v[16];
 #pragma unroll
     for (int k = 0; k < 16; ++k)
       v[k] = *(const __attribute__((address_space(3))) i32x4*)(stage + (r0 + 2 * k + hi) * kStageRowBytes + (lane & 31) * 16);
     __builtin_amdgcn_sched_barrier(0);
+    // (written through: the merge reads the partials from another XCD, not from this L2)
+    if (full_group) {
+      char* rowp = (char*)(part_base + (int64_t)(grow0 + hi) * kDv);
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const int grow = grow0 + 2 * k + hi;
-      // (written through: the merge reads the partials from another XCD, not from this L2)
-      if (grow < R) store16_through(part_base + (int64_t)grow * kDv, v[k]);
-      between(k);
-      __builtin_amdgcn_sched_barrier(0);
+      for (int k = 0; k < 16; ++k) {  // row grow0 + 2k + hi: (k / 2) * 4 KiB + (k % 2) * 2 KiB from rowp
+        if (k & 1) store16_through_at<2 * kDv * 2>(rowp + (k >> 1) * 4 * kDv * 2, v[k]);
+        else store16_through_at<0>(rowp + (k >> 1) * 4 * kDv * 2, v[k]);
+        between(k);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const int grow = grow0 + 2 * k + hi;
+        if (grow < R) store16_through(part_base + (int64_t)grow * kDv, v[k]);
+        between(k);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   };
 #pragma unroll
